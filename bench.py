@@ -1,0 +1,192 @@
+"""Benchmark of the gfx950 fp16/fp32-accumulate GEMM (one JSON line on stdout).
+
+A step is one C = A B over the whole workload (default: 8192 x 8192 x 8192, A and B
+uniform on [-0.5, 0.5), seed 3), with A and B already resident in HBM.  W warm-up steps,
+then K timed steps bracketed by device synchronisation.  Per-launch durations come from
+HIP events recorded on the stream the kernel is launched on (torch's current stream).
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--all]
+                    [--tile T] [--group-m G] [--xcd-remap R] [--no-cpu-baseline]
+
+`value` is TFLOP/s = 2 M N K K_steps / (timed wall time); `roofline.achieved` is
+2 M N K / (mean per-launch event time), against the MI355X published dense fp16 matrix
+peak of 2.5 PFLOP/s.  `cpu_baseline` times the CPU oracle (fp64 ascending-k sums, one
+rounding) on one 256-row band of the same product, using all host threads it gets.
+--all prints one extra JSON line per workload to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "fp16-in/fp32-acc GEMM TFLOP/s at 8192³ on 1 MI355X; % of fp16 MFMA peak"
+PEAK_TFLOPS = 2500.0          # MI355X published dense fp16 matrix peak
+CSRC = os.path.join(ROOT, "dense_gemm_f16f32_amd", "csrc")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str, tile: int, group_m: int, remap: int):
+    """HBM bytes per launch from the committed rocprofv3 counter runs, or None when they
+    were taken for another kernel source or launch configuration."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    key = f"{workload}/tile{tile}/g{group_m}/remap{remap}"
+    e = rec.get(key)
+    if not e or e.get("source_hash") != kernel_source_hash():
+        return None
+    return e.get("bytes_per_launch")
+
+
+def time_workload(g, torch, name, steps, warmup, opts):
+    import numpy as np
+    from synthetic_inputs import operands, workload
+
+    _, M, N, K, dist, seed = workload(name)
+    A, B = operands(M, N, K, dist, seed)
+    Ad = torch.from_numpy(A.view(np.int16)).cuda()
+    Bd = torch.from_numpy(B.view(np.int16)).cuda()
+    Cd = torch.empty((M, N), dtype=torch.int16, device="cuda")
+    del A, B
+    rc, plan = g.gemm_f16f32_plan(M, N, K, Ad.data_ptr(), Bd.data_ptr(), Cd.data_ptr(), K, N, N,
+                                  opts=opts or None)
+    if rc != g.OK:
+        raise g.GemmError(rc, "plan")
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        g.matmul(Ad, Bd, Cd, **opts)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s, e in ev:
+        s.record(stream)
+        g.matmul(Ad, Bd, Cd, **opts)
+        e.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = sorted(s.elapsed_time(e) for s, e in ev)      # ms
+    flops = 2.0 * M * N * K
+    mean_ms = sum(per) / len(per)
+    return {
+        "workload": name, "M": M, "N": N, "K": K, "plan": plan,
+        "value": flops * steps / wall / 1e12, "ms_per_step": wall * 1e3 / steps,
+        "kernel_ms_mean": mean_ms, "kernel_ms_median": per[len(per) // 2],
+        "kernel_ms_min": per[0], "kernel_ms_p90": per[min(len(per) - 1, int(0.9 * len(per)))],
+        "achieved_tflops": flops / (mean_ms * 1e-3) / 1e12,
+    }
+
+
+def cpu_baseline(name: str, rows: int = 256):
+    import numpy as np
+    import oracle
+    from synthetic_inputs import operands, workload
+
+    _, M, N, K, dist, seed = workload(name)
+    A, B = operands(M, N, K, dist, seed)
+    rows = min(rows, M)
+    Ab = np.ascontiguousarray(A[:rows])
+    del A
+    oracle.lib()
+    t0 = time.perf_counter()
+    oracle.gemm(Ab, B)
+    dt = time.perf_counter() - t0
+    return {"value": 2.0 * rows * N * K / dt / 1e12, "unit": "TFLOP/s",
+            "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"rows 0..{rows - 1} of C ({rows} x {N} outputs, K = {K}) of {name}, "
+                      f"{dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="gemm8192_u")
+    ap.add_argument("--all", action="store_true", help="also time every workload (stderr)")
+    ap.add_argument("--tile", type=int, default=0)
+    ap.add_argument("--group-m", type=int, default=0)
+    ap.add_argument("--xcd-remap", type=int, default=0)
+    ap.add_argument("--force-generic", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the GEMM runs on a single MI355X and this build "
+              "has no multi-GPU path (run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import dense_gemm_f16f32_amd as g
+    from synthetic_inputs import WORKLOADS
+
+    torch.cuda.set_device(0)
+    opts = {k: v for k, v in (("tile", args.tile), ("group_m", args.group_m),
+                              ("xcd_remap", args.xcd_remap),
+                              ("force_generic", args.force_generic)) if v}
+
+    if args.all:
+        for w in WORKLOADS:
+            small = w[1] * w[2] * w[3] < 1 << 31
+            r = time_workload(g, torch, w[0], 1000 if small else 50, 10, opts)
+            r["frac_of_peak"] = r["achieved_tflops"] / PEAK_TFLOPS
+            print(json.dumps(r), file=sys.stderr, flush=True)
+
+    r = time_workload(g, torch, args.workload, args.steps, args.warmup, opts)
+    plan = r["plan"]
+    traffic = measured_traffic(args.workload, plan["tile"], plan["group_m"], plan["xcd_remap"])
+    out = {
+        "metric": METRIC,
+        "value": round(r["value"], 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {
+            "workload": args.workload, "M": r["M"], "N": r["N"], "K": r["K"],
+            "accumulate": "f32", "path": ["aligned", "generic"][plan["path"]],
+            "tile": f"{plan['bm']}x{plan['bn']}x{plan['bk']}", "group_m": plan["group_m"],
+            "xcd_remap": plan["xcd_remap"], "workgroups": plan["num_programs"],
+        },
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(r["achieved_tflops"], 2),
+            "peak": PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(r["achieved_tflops"] / PEAK_TFLOPS, 4),
+            "traffic": traffic,
+            "kernel_ms": {k: round(r["kernel_ms_" + k], 5) for k in ("mean", "median", "min",
+                                                                      "p90")},
+        },
+        "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline(args.workload),
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,168 @@
+"""Python binding of libgemm_f16f32.so (the gfx950 fp16/fp32-accumulate GEMM).
+
+The functions named like the C-ABI (gemm_f16f32, gemm_f16f32_ex, gemm_f16f32_plan,
+gemm_f16f32_tile_map, gemm_f16f32_strerror, gemm_f16f32_version) only marshal arguments
+into the library; every step of the computation runs in its HIP kernels.  `matmul` is the
+same call for torch tensors: it passes their device pointers, leading dimensions and
+torch's current HIP stream.  PyTorch is used for device memory and streams only.
+
+The library is loaded on first use; if it has not been built the call raises at once
+(there is no fallback of any kind).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libgemm_f16f32.so")
+
+OK = 0
+ERR_DIM, ERR_NULL, ERR_LD, ERR_OVERLAP, ERR_OPTS, ERR_TOO_LARGE, ERR_HIP = range(-1, -8, -1)
+TILE_AUTO, TILE_256x256x64, TILE_128x128x64, TILE_128x64x64, TILE_256x128x64 = range(5)
+TILES = {TILE_256x256x64: (256, 256), TILE_128x128x64: (128, 128), TILE_128x64x64: (128, 64),
+         TILE_256x128x64: (256, 128)}
+PATH_ALIGNED, PATH_GENERIC = 0, 1
+REMAP_DEFAULT, REMAP_ON, REMAP_OFF = 0, 1, 2
+
+
+class GemmError(RuntimeError):
+    def __init__(self, code: int, what: str = ""):
+        self.code = code
+        super().__init__(f"{what}: {gemm_f16f32_strerror(code)} (code {code})")
+
+
+class Opts(ctypes.Structure):
+    _fields_ = [("tile", ctypes.c_int32), ("group_m", ctypes.c_int32),
+                ("xcd_remap", ctypes.c_int32), ("force_generic", ctypes.c_int32)]
+
+
+class PlanInfo(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("path", "tile", "bm", "bn", "bk", "group_m",
+                                              "xcd_remap", "num_pid_m", "num_pid_n",
+                                              "num_programs")]
+
+    def as_dict(self) -> dict:
+        return {n: getattr(self, n) for n, _ in self._fields_}
+
+
+_lib = None
+_i64 = ctypes.c_int64
+_vp = ctypes.c_void_p
+_GEMM_ARGS = [_i64, _i64, _i64, _vp, _vp, _vp, _i64, _i64, _i64]
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises if libgemm_f16f32.so has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                               "(or python dense_gemm_f16f32_amd/build.py)")
+        L = ctypes.CDLL(LIB_PATH)
+        L.gemm_f16f32.argtypes = _GEMM_ARGS + [_vp]
+        L.gemm_f16f32.restype = ctypes.c_int
+        L.gemm_f16f32_ex.argtypes = _GEMM_ARGS + [_vp, ctypes.POINTER(Opts)]
+        L.gemm_f16f32_ex.restype = ctypes.c_int
+        L.gemm_f16f32_plan.argtypes = _GEMM_ARGS + [ctypes.POINTER(Opts),
+                                                    ctypes.POINTER(PlanInfo)]
+        L.gemm_f16f32_plan.restype = ctypes.c_int
+        L.gemm_f16f32_tile_map.argtypes = [ctypes.c_int32] * 4 + [_vp, _vp]
+        L.gemm_f16f32_tile_map.restype = ctypes.c_int
+        L.gemm_f16f32_strerror.argtypes = [ctypes.c_int]
+        L.gemm_f16f32_strerror.restype = ctypes.c_char_p
+        L.gemm_f16f32_version.argtypes = []
+        L.gemm_f16f32_version.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _opts(opts) -> Opts | None:
+    if opts is None or isinstance(opts, Opts):
+        return opts
+    return Opts(**opts)
+
+
+# ---- C-ABI names: plain integers for pointers and the stream handle -----------------------
+
+def gemm_f16f32(M, N, K, A, B, C, lda, ldb, ldc, stream=None) -> int:
+    return lib().gemm_f16f32(M, N, K, A, B, C, lda, ldb, ldc, stream)
+
+
+def gemm_f16f32_ex(M, N, K, A, B, C, lda, ldb, ldc, stream=None, opts=None) -> int:
+    o = _opts(opts)
+    return lib().gemm_f16f32_ex(M, N, K, A, B, C, lda, ldb, ldc, stream,
+                                ctypes.byref(o) if o is not None else None)
+
+
+def gemm_f16f32_plan(M, N, K, A, B, C, lda, ldb, ldc, opts=None):
+    """(code, dict of the plan) -- host only, nothing is launched."""
+    o = _opts(opts)
+    info = PlanInfo()
+    rc = lib().gemm_f16f32_plan(M, N, K, A, B, C, lda, ldb, ldc,
+                                ctypes.byref(o) if o is not None else None, ctypes.byref(info))
+    return rc, (info.as_dict() if rc == OK else None)
+
+
+def gemm_f16f32_tile_map(num_pid_m, num_pid_n, group_m, xcd_remap, out_dev, stream=None) -> int:
+    return lib().gemm_f16f32_tile_map(num_pid_m, num_pid_n, group_m, xcd_remap, out_dev, stream)
+
+
+def gemm_f16f32_strerror(code: int) -> str:
+    return lib().gemm_f16f32_strerror(code).decode()
+
+
+def gemm_f16f32_version() -> int:
+    return lib().gemm_f16f32_version()
+
+
+# ---- torch tensors -------------------------------------------------------------------------
+
+def _ld(t) -> int:
+    if t.dim() != 2:
+        raise ValueError("expected a 2-D tensor")
+    if t.numel() and t.stride(1) != 1:
+        raise ValueError("expected unit stride along rows")
+    return max(t.stride(0), t.shape[1], 1)
+
+
+def _stream_handle(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def matmul(a, b, out=None, *, M=None, N=None, K=None, stream=None, **opts):
+    """out[:M, :N] = fp16(a[:M, :K] @ b[:K, :N]) on the GPU (fp32 accumulation).
+
+    a, b, out: 2-D CUDA tensors of 16-bit elements (float16, or int16 holding fp16 bits),
+    row-major with unit inner stride and any leading dimension.  opts: tile, group_m,
+    xcd_remap, force_generic (see include/gemm_f16f32.h).  Raises GemmError on a non-zero
+    return code.  Launches on torch's current stream unless `stream` is given.
+    """
+    import torch
+    M = a.shape[0] if M is None else M
+    K = a.shape[1] if K is None else K
+    N = b.shape[1] if N is None else N
+    if out is None:
+        out = torch.empty((M, N), dtype=a.dtype, device=a.device)
+    for t in (a, b, out):
+        if t.element_size() != 2 or not t.is_cuda:
+            raise ValueError("operands must be 16-bit CUDA tensors")
+    rc = gemm_f16f32_ex(M, N, K, a.data_ptr(), b.data_ptr(), out.data_ptr(), _ld(a), _ld(b),
+                        _ld(out), _stream_handle(stream), Opts(**opts) if opts else None)
+    if rc != OK:
+        raise GemmError(rc, "gemm_f16f32_ex")
+    return out
+
+
+def tile_map(num_pid_m, num_pid_n, group_m, xcd_remap, stream=None):
+    """(P, 3) int32 CUDA tensor from gemm_f16f32_tile_map: (logical pid, pid_m, pid_n)."""
+    import torch
+    P = num_pid_m * num_pid_n
+    out = torch.full((P, 3), -1, dtype=torch.int32, device="cuda")
+    rc = gemm_f16f32_tile_map(num_pid_m, num_pid_n, group_m, xcd_remap, out.data_ptr(),
+                              _stream_handle(stream))
+    if rc != OK:
+        raise GemmError(rc, "gemm_f16f32_tile_map")
+    return out

@@ -1,0 +1,196 @@
+// C-ABI of the gfx950 fp16/fp32-accumulate GEMM: argument checks, kernel choice, launch.
+// The declarations and their contracts are in include/gemm_f16f32.h.
+#include "gemm_f16f32.h"
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gemm_kernels.hpp"
+
+namespace {
+
+constexpr int kVersion = 100;  // 0.1.0
+
+struct TileDesc {
+  int id, bm, bn, default_group;
+};
+
+constexpr TileDesc kTiles[] = {
+    {GEMM_F16F32_TILE_256x256x64, 256, 256, 8},
+    {GEMM_F16F32_TILE_128x128x64, 128, 128, 4},
+    {GEMM_F16F32_TILE_128x64x64, 128, 64, 4},
+    {GEMM_F16F32_TILE_256x128x64, 256, 128, 8},
+};
+
+const TileDesc* find_tile(int id) {
+  for (const TileDesc& t : kTiles)
+    if (t.id == id) return &t;
+  return nullptr;
+}
+
+int64_t cdiv(int64_t x, int64_t y) { return (x + y - 1) / y; }
+
+// Tile chosen from the shape: the largest tile whose grid still covers the 256 CUs about
+// once; smaller problems fall back to smaller tiles so that more CUs take part.
+int auto_tile(int64_t M, int64_t N) {
+  if (cdiv(M, 256) * cdiv(N, 256) >= 240) return GEMM_F16F32_TILE_256x256x64;
+  if (cdiv(M, 256) * cdiv(N, 128) >= 240) return GEMM_F16F32_TILE_256x128x64;
+  if (cdiv(M, 128) * cdiv(N, 128) >= 120) return GEMM_F16F32_TILE_128x128x64;
+  return GEMM_F16F32_TILE_128x64x64;
+}
+
+// Bytes from a matrix's first element to one past its last, for rows x cols at leading
+// dimension ld (0 if empty).
+uint64_t footprint(int64_t rows, int64_t cols, int64_t ld) {
+  if (rows <= 0 || cols <= 0) return 0;
+  return 2ull * (uint64_t)((rows - 1) * ld + cols);
+}
+
+bool overlaps(const void* a, uint64_t na, const void* b, uint64_t nb) {
+  if (na == 0 || nb == 0) return false;
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return x < y + nb && y < x + na;
+}
+
+int plan(int64_t M, int64_t N, int64_t K, const uint16_t* A, const uint16_t* B,
+         const uint16_t* C, int64_t lda, int64_t ldb, int64_t ldc, const gemm_f16f32_opts* opts,
+         gemm_f16f32_plan_info* info) {
+  const int64_t kMax = (int64_t)1 << 31;
+  if (M < 0 || N < 0 || K < 0 || M >= kMax || N >= kMax || K >= kMax) return GEMM_F16F32_ERR_DIM;
+  if (lda < (K > 1 ? K : 1) || ldb < (N > 1 ? N : 1) || ldc < (N > 1 ? N : 1))
+    return GEMM_F16F32_ERR_LD;
+  const bool emptyC = (M == 0 || N == 0);
+  if (!emptyC && C == nullptr) return GEMM_F16F32_ERR_NULL;
+  if (!emptyC && K > 0 && (A == nullptr || B == nullptr)) return GEMM_F16F32_ERR_NULL;
+  if (((uintptr_t)A | (uintptr_t)B | (uintptr_t)C) & 1) return GEMM_F16F32_ERR_OPTS;
+
+  gemm_f16f32_opts o = {0, 0, 0, 0};
+  if (opts) o = *opts;
+  if (o.tile != 0 && find_tile(o.tile) == nullptr) return GEMM_F16F32_ERR_OPTS;
+  if (o.group_m < 0 || o.xcd_remap < 0 || o.xcd_remap > 2 || o.force_generic < 0 ||
+      o.force_generic > 1)
+    return GEMM_F16F32_ERR_OPTS;
+
+  if (!emptyC) {
+    const uint64_t fc = footprint(M, N, ldc);
+    if (overlaps(C, fc, A, footprint(M, K, lda)) || overlaps(C, fc, B, footprint(K, N, ldb)))
+      return GEMM_F16F32_ERR_OVERLAP;
+  }
+
+  const TileDesc* t = find_tile(o.tile ? o.tile : auto_tile(M, N));
+  // 32-bit in-kernel offsets: one panel's rows of A (bm x lda) and of B (64 x ldb).
+  if ((int64_t)t->bm * lda >= kMax || (int64_t)gk::kBK * ldb >= kMax) return GEMM_F16F32_ERR_TOO_LARGE;
+
+  const bool aligned = !o.force_generic && ((uintptr_t)A % 16 == 0) && ((uintptr_t)B % 16 == 0) &&
+                       lda % 8 == 0 && ldb % 8 == 0 && N % 8 == 0 && K % gk::kBK == 0;
+  gemm_f16f32_plan_info r;
+  r.path = aligned ? GEMM_F16F32_PATH_ALIGNED : GEMM_F16F32_PATH_GENERIC;
+  r.tile = t->id;
+  r.bm = t->bm;
+  r.bn = t->bn;
+  r.bk = gk::kBK;
+  r.group_m = o.group_m ? o.group_m : t->default_group;
+  r.xcd_remap = (o.xcd_remap == 2) ? 0 : 1;
+  r.num_pid_m = emptyC ? 0 : (int32_t)cdiv(M, t->bm);
+  r.num_pid_n = emptyC ? 0 : (int32_t)cdiv(N, t->bn);
+  const int64_t P = (int64_t)r.num_pid_m * r.num_pid_n;
+  if (P >= kMax) return GEMM_F16F32_ERR_TOO_LARGE;
+  r.num_programs = (int32_t)P;
+  if (info) *info = r;
+  return GEMM_F16F32_OK;
+}
+
+template <int BM, int BN>
+hipError_t launch(const gemm_f16f32_plan_info& r, const gk::Args& a, bool odd,
+                  hipStream_t stream) {
+  const dim3 grid(r.num_programs), block(gk::kThreads);
+  if (r.path == GEMM_F16F32_PATH_ALIGNED)
+    hipLaunchKernelGGL((gk::gemm_aligned<BM, BN>), grid, block, 0, stream, a);
+  else if (odd)
+    hipLaunchKernelGGL((gk::gemm_generic<BM, BN, true>), grid, block, 0, stream, a);
+  else
+    hipLaunchKernelGGL((gk::gemm_generic<BM, BN, false>), grid, block, 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+extern "C" {
+
+int gemm_f16f32_plan(int64_t M, int64_t N, int64_t K, const uint16_t* A, const uint16_t* B,
+                     const uint16_t* C, int64_t lda, int64_t ldb, int64_t ldc,
+                     const gemm_f16f32_opts* opts, gemm_f16f32_plan_info* info) {
+  return plan(M, N, K, A, B, C, lda, ldb, ldc, opts, info);
+}
+
+int gemm_f16f32_ex(int64_t M, int64_t N, int64_t K, const uint16_t* A, const uint16_t* B,
+                   uint16_t* C, int64_t lda, int64_t ldb, int64_t ldc, void* stream,
+                   const gemm_f16f32_opts* opts) {
+  gemm_f16f32_plan_info r;
+  const int rc = plan(M, N, K, A, B, C, lda, ldb, ldc, opts, &r);
+  if (rc != GEMM_F16F32_OK) return rc;
+  if (r.num_programs == 0) return GEMM_F16F32_OK;
+
+  gk::Args a;
+  a.A = A;
+  a.B = B;
+  a.C = C;
+  a.lda = lda;
+  a.ldb = ldb;
+  a.ldc = ldc;
+  a.M = (int32_t)M;
+  a.N = (int32_t)N;
+  a.K = (int32_t)K;
+  a.num_pid_m = r.num_pid_m;
+  a.num_pid_n = r.num_pid_n;
+  a.group_m = r.group_m;
+  a.xcd_remap = r.xcd_remap;
+  a.num_programs = r.num_programs;
+  const bool odd = (((uintptr_t)A | (uintptr_t)B) & 3) != 0 || ((lda | ldb) & 1) != 0;
+  hipStream_t s = (hipStream_t)stream;
+
+  hipError_t e = hipSuccess;
+  switch (r.tile) {
+    case GEMM_F16F32_TILE_256x256x64: e = launch<256, 256>(r, a, odd, s); break;
+    case GEMM_F16F32_TILE_256x128x64: e = launch<256, 128>(r, a, odd, s); break;
+    case GEMM_F16F32_TILE_128x128x64: e = launch<128, 128>(r, a, odd, s); break;
+    case GEMM_F16F32_TILE_128x64x64: e = launch<128, 64>(r, a, odd, s); break;
+    default: return GEMM_F16F32_ERR_OPTS;
+  }
+  return e == hipSuccess ? GEMM_F16F32_OK : GEMM_F16F32_ERR_HIP;
+}
+
+int gemm_f16f32(int64_t M, int64_t N, int64_t K, const uint16_t* A, const uint16_t* B,
+                uint16_t* C, int64_t lda, int64_t ldb, int64_t ldc, void* stream) {
+  return gemm_f16f32_ex(M, N, K, A, B, C, lda, ldb, ldc, stream, nullptr);
+}
+
+int gemm_f16f32_tile_map(int32_t num_pid_m, int32_t num_pid_n, int32_t group_m,
+                         int32_t xcd_remap, int32_t* out_dev, void* stream) {
+  if (num_pid_m < 1 || num_pid_n < 1) return GEMM_F16F32_ERR_DIM;
+  const int64_t P = (int64_t)num_pid_m * num_pid_n;
+  if (P >= ((int64_t)1 << 31)) return GEMM_F16F32_ERR_DIM;
+  if (group_m < 1 || xcd_remap < 0 || xcd_remap > 2) return GEMM_F16F32_ERR_OPTS;
+  if (out_dev == nullptr) return GEMM_F16F32_ERR_NULL;
+  hipLaunchKernelGGL(gk::tile_map_kernel, dim3((uint32_t)P), dim3(64), 0, (hipStream_t)stream,
+                     (int)P, num_pid_m, num_pid_n, group_m, xcd_remap == 1 ? 1 : 0, out_dev);
+  return hipGetLastError() == hipSuccess ? GEMM_F16F32_OK : GEMM_F16F32_ERR_HIP;
+}
+
+const char* gemm_f16f32_strerror(int code) {
+  switch (code) {
+    case GEMM_F16F32_OK: return "success";
+    case GEMM_F16F32_ERR_DIM: return "M, N or K negative or too large";
+    case GEMM_F16F32_ERR_NULL: return "NULL pointer for a non-empty operand";
+    case GEMM_F16F32_ERR_LD: return "leading dimension smaller than the row length";
+    case GEMM_F16F32_ERR_OVERLAP: return "C overlaps A or B";
+    case GEMM_F16F32_ERR_OPTS: return "invalid option or misaligned pointer";
+    case GEMM_F16F32_ERR_TOO_LARGE: return "leading dimension too large for 32-bit tile offsets";
+    case GEMM_F16F32_ERR_HIP: return "HIP runtime rejected the launch";
+    default: return "unknown error code";
+  }
+}
+
+int gemm_f16f32_version(void) { return kVersion; }
+
+}  // extern "C"

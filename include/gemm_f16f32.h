@@ -1,0 +1,138 @@
+/*
+ * gemm_f16f32: C = A B on one MI355X (gfx950), fp16 operands, fp32 accumulation, one
+ * narrowing to fp16 on the store, output tiles visited in grouped GROUP_SIZE_M order.
+ *
+ * The operation is the matmul of phobos "03: Matrix multiplication" (the `matmul` kernel,
+ * its docstring and the paragraph after it): A is M x K, B is K x N, C is M x N, every
+ * element C[i][j] is the fp32 sum over k of A[i][k] * B[k][j], rounded once to fp16 (round
+ * to nearest, ties to even, as a `.to(float16)` narrowing does).  Inside fp32 the order of
+ * the k-sum is the kernel's own; results agree with the exactly rounded sum within
+ * 1e-2 + 2^-10 |C| element-wise.  There is no alpha/beta: C is overwritten, never read.
+ *
+ * The launch order of output tiles is the grouped order of the kernl notebook "Computing
+ * coordinates on Triton GEMM example" (introduction excerpt, cells In[1]-In[7]): with
+ * num_pid_m = cdiv(M, BM) and num_pid_n = cdiv(N, BN) tiles per axis, program pid belongs to
+ * group pid / (G * num_pid_n), groups cover G tile-rows (the last one may be smaller) and
+ * programs inside a group run column-major.  Before that map the hardware workgroup id may
+ * be permuted so that consecutive program ids share one XCD's L2 (gemm_f16f32_tile_map
+ * documents the permutation).
+ *
+ * Layout: all matrices are row-major with unit stride along a row and a leading dimension
+ * (elements between the starts of consecutive rows): A[i][k] is at A + i*lda + k, B[k][j] at
+ * B + k*ldb + j, C[i][j] at C + i*ldc + j (the stride convention of the notebook's cell
+ * In[8]).  Values are IEEE binary16 bit patterns passed as uint16_t.
+ *
+ * Ownership and execution: A, B, C are device pointers owned by the caller.  The library
+ * allocates nothing and keeps no state between calls, so calls from several host threads are
+ * safe.  A call checks its arguments, launches on `stream` (a hipStream_t; NULL is the null
+ * stream) and returns without waiting; faults inside a kernel surface at the caller's next
+ * synchronisation.  Only C[i][j] with i < M, j < N is written (padding between N and ldc is
+ * left as it was).  M == 0 or N == 0 is a successful no-op; K == 0 writes +0 to the M x N
+ * block.
+ *
+ * Errors: every entry point returns GEMM_F16F32_OK (0) or a negative code; argument errors
+ * are found on the host before anything is launched.
+ */
+#ifndef GEMM_F16F32_H
+#define GEMM_F16F32_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    GEMM_F16F32_OK = 0,
+    GEMM_F16F32_ERR_DIM = -1,       /* M, N or K negative, or >= 2^31 */
+    GEMM_F16F32_ERR_NULL = -2,      /* a NULL pointer for a non-empty operand */
+    GEMM_F16F32_ERR_LD = -3,        /* lda < max(K,1), ldb < max(N,1) or ldc < max(N,1) */
+    GEMM_F16F32_ERR_OVERLAP = -4,   /* C's footprint overlaps A's or B's */
+    GEMM_F16F32_ERR_OPTS = -5,      /* an option outside its range, or an odd pointer address */
+    GEMM_F16F32_ERR_TOO_LARGE = -6, /* a leading dimension beyond the kernels' 32-bit offsets */
+    GEMM_F16F32_ERR_HIP = -7        /* the HIP runtime rejected the launch */
+};
+
+/* Tile configurations (BM x BN x BK; 256 threads = 4 wavefronts of 64 lanes in a 2 x 2
+ * arrangement, each accumulating a (BM/2) x (BN/2) block with 32x32x16 fp16 MFMAs). */
+enum {
+    GEMM_F16F32_TILE_AUTO = 0,
+    GEMM_F16F32_TILE_256x256x64 = 1,
+    GEMM_F16F32_TILE_128x128x64 = 2,
+    GEMM_F16F32_TILE_128x64x64 = 3,
+    GEMM_F16F32_TILE_256x128x64 = 4
+};
+
+/* Kernel families. */
+enum {
+    GEMM_F16F32_PATH_ALIGNED = 0, /* 16-byte aligned A/B, lda/ldb % 8 == 0, N % 8 == 0,
+                                     K % BK == 0: 128-bit direct global->LDS loads */
+    GEMM_F16F32_PATH_GENERIC = 1  /* anything else: bounds-checked buffer loads, K-tail
+                                     zero fill, any leading dimension and alignment */
+};
+
+/* Options for gemm_f16f32_ex.  Zero-initialised options mean "library default" throughout. */
+typedef struct gemm_f16f32_opts {
+    int32_t tile;          /* GEMM_F16F32_TILE_*; 0 = chosen from the shape */
+    int32_t group_m;       /* GROUP_SIZE_M >= 1; 0 = library default for the tile */
+    int32_t xcd_remap;     /* 0 = default (on), 1 = on, 2 = off (hardware id = program id) */
+    int32_t force_generic; /* 1 = use the generic path even when the aligned one applies */
+} gemm_f16f32_opts;
+
+/* What a call with these arguments would launch (filled by gemm_f16f32_plan). */
+typedef struct gemm_f16f32_plan_info {
+    int32_t path;          /* GEMM_F16F32_PATH_* */
+    int32_t tile;          /* GEMM_F16F32_TILE_* actually used */
+    int32_t bm, bn, bk;    /* tile sizes */
+    int32_t group_m;       /* GROUP_SIZE_M actually used */
+    int32_t xcd_remap;     /* 1 if the XCD permutation is applied */
+    int32_t num_pid_m;     /* cdiv(M, bm) */
+    int32_t num_pid_n;     /* cdiv(N, bn) */
+    int32_t num_programs;  /* num_pid_m * num_pid_n = workgroups launched (0 if none) */
+} gemm_f16f32_plan_info;
+
+/*
+ * C[0:M, 0:N] = fp16( A[0:M, 0:K] . B[0:K, 0:N] ), fp32 accumulation, default options.
+ * M, N, K: problem sizes (>= 0).  A, B, C: device pointers (see Layout).  lda >= max(K,1),
+ * ldb >= max(N,1), ldc >= max(N,1).  stream: hipStream_t or NULL.
+ */
+int gemm_f16f32(int64_t M, int64_t N, int64_t K, const uint16_t *A, const uint16_t *B,
+                uint16_t *C, int64_t lda, int64_t ldb, int64_t ldc, void *stream);
+
+/* Same as gemm_f16f32 with explicit options (opts may be NULL = defaults). */
+int gemm_f16f32_ex(int64_t M, int64_t N, int64_t K, const uint16_t *A, const uint16_t *B,
+                   uint16_t *C, int64_t lda, int64_t ldb, int64_t ldc, void *stream,
+                   const gemm_f16f32_opts *opts);
+
+/* Host only, no GPU work: validates like gemm_f16f32_ex and reports in *info which kernel,
+ * tile, GROUP_SIZE_M and grid that call would use.  Pointers are inspected for alignment and
+ * overlap only, never dereferenced. */
+int gemm_f16f32_plan(int64_t M, int64_t N, int64_t K, const uint16_t *A, const uint16_t *B,
+                     const uint16_t *C, int64_t lda, int64_t ldb, int64_t ldc,
+                     const gemm_f16f32_opts *opts, gemm_f16f32_plan_info *info);
+
+/*
+ * Writes, for every hardware workgroup id h in [0, P), P = num_pid_m * num_pid_n, the
+ * triple (logical program id, pid_m, pid_n) to out_dev[3h], out_dev[3h+1], out_dev[3h+2]
+ * (device memory, 3P int32 owned by the caller), computed on the GPU by the same device
+ * function the GEMM kernels use.  xcd_remap 1: logical id = x*q + min(x, r) + h/8 with
+ * x = h % 8, q = P / 8, r = P % 8 (the 8 XCDs receive workgroups round-robin, so each XCD's
+ * workgroups get one contiguous run of program ids); xcd_remap 0 (or 2): logical id = h.
+ * The grouped map of the kernl notebook's introduction excerpt then gives (pid_m, pid_n).
+ * Errors: GEMM_F16F32_ERR_DIM if a size is < 1 or P >= 2^31, ERR_OPTS for group_m < 1 or
+ * xcd_remap outside 0..2, ERR_NULL for a NULL out_dev, ERR_HIP for a rejected launch.
+ */
+int gemm_f16f32_tile_map(int32_t num_pid_m, int32_t num_pid_n, int32_t group_m,
+                         int32_t xcd_remap, int32_t *out_dev, void *stream);
+
+/* Static description of an error code (never NULL). */
+const char *gemm_f16f32_strerror(int code);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int gemm_f16f32_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GEMM_F16F32_H */

@@ -1,0 +1,122 @@
+"""Host-side checks of libgemm_f16f32.so that need no GPU.
+
+The library loads, exports every function include/gemm_f16f32.h declares, rejects bad
+arguments with the documented codes before touching the GPU, and plans the documented kernel
+path, tile, GROUP_SIZE_M and grid.  No call here launches a kernel.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import dense_gemm_f16f32_amd as g
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gemm_f16f32.h")
+
+# Fake, never dereferenced device addresses (16-byte aligned, far apart).
+PA, PB, PC = 0x10000000, 0x20000000, 0x30000000
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gemm_f16f32\w*)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    names = declared_functions()
+    assert "gemm_f16f32" in names and "gemm_f16f32_tile_map" in names
+    L = ctypes.CDLL(g.LIB_PATH)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_version_and_strerror():
+    assert g.gemm_f16f32_version() >= 100
+    for code in [0, -1, -2, -3, -4, -5, -6, -7]:
+        assert g.gemm_f16f32_strerror(code) and g.gemm_f16f32_strerror(code) != "unknown error code"
+    assert g.gemm_f16f32_strerror(-99) == "unknown error code"
+
+
+@pytest.mark.parametrize("args,code", [
+    ((-1, 8, 8, PA, PB, PC, 8, 8, 8), g.ERR_DIM),
+    ((8, -1, 8, PA, PB, PC, 8, 8, 8), g.ERR_DIM),
+    ((8, 8, -1, PA, PB, PC, 8, 8, 8), g.ERR_DIM),
+    ((1 << 31, 8, 8, PA, PB, PC, 8, 8, 8), g.ERR_DIM),
+    ((8, 8, 8, PA, PB, PC, 7, 8, 8), g.ERR_LD),
+    ((8, 8, 8, PA, PB, PC, 8, 7, 8), g.ERR_LD),
+    ((8, 8, 8, PA, PB, PC, 8, 8, 7), g.ERR_LD),
+    ((8, 8, 0, PA, PB, PC, 0, 8, 8), g.ERR_LD),
+    ((8, 8, 8, 0, PB, PC, 8, 8, 8), g.ERR_NULL),
+    ((8, 8, 8, PA, 0, PC, 8, 8, 8), g.ERR_NULL),
+    ((8, 8, 8, PA, PB, 0, 8, 8, 8), g.ERR_NULL),
+    ((8, 8, 8, PA, PB, PA + 16, 8, 8, 8), g.ERR_OVERLAP),
+    ((8, 8, 8, PA, PB, PB + 126, 8, 8, 8), g.ERR_OVERLAP),
+    ((8, 8, 8, PA + 1, PB, PC, 8, 8, 8), g.ERR_OPTS),
+    ((8, 8, 8, PA, PB, PC, 1 << 24, 8, 8), g.ERR_TOO_LARGE),
+])
+def test_argument_errors_before_launch(args, code):
+    assert g.gemm_f16f32(*args, None) == code
+    rc, _ = g.gemm_f16f32_plan(*args)
+    assert rc == code
+
+
+def test_empty_problems_are_noops():
+    # M == 0 or N == 0: success without any GPU call (no device here), NULL pointers allowed.
+    assert g.gemm_f16f32(0, 8, 8, 0, 0, 0, 8, 8, 8, None) == g.OK
+    assert g.gemm_f16f32(8, 0, 8, 0, 0, 0, 8, 1, 1, None) == g.OK
+    rc, info = g.gemm_f16f32_plan(0, 8, 8, 0, 0, 0, 8, 8, 8)
+    assert rc == g.OK and info["num_programs"] == 0
+    # K == 0 needs C only
+    rc, info = g.gemm_f16f32_plan(8, 8, 0, 0, 0, PC, 1, 8, 8)
+    assert rc == g.OK and info["num_programs"] > 0
+
+
+def test_option_errors():
+    base = (64, 64, 64, PA, PB, PC, 64, 64, 64)
+    for bad in ({"tile": 9}, {"group_m": -1}, {"xcd_remap": 3}, {"force_generic": 2}):
+        assert g.gemm_f16f32_plan(*base, opts=bad)[0] == g.ERR_OPTS
+        assert g.gemm_f16f32_ex(*base, None, bad) == g.ERR_OPTS
+
+
+def test_tile_map_argument_errors():
+    assert g.gemm_f16f32_tile_map(0, 4, 1, 0, PC) == g.ERR_DIM
+    assert g.gemm_f16f32_tile_map(4, 4, 0, 0, PC) == g.ERR_OPTS
+    assert g.gemm_f16f32_tile_map(4, 4, 1, 3, PC) == g.ERR_OPTS
+    assert g.gemm_f16f32_tile_map(4, 4, 1, 0, 0) == g.ERR_NULL
+    assert g.gemm_f16f32_tile_map(1 << 16, 1 << 16, 1, 0, PC) == g.ERR_DIM
+
+
+def plan(M, N, K, lda=None, ldb=None, ldc=None, a=PA, b=PB, c=PC, **opts):
+    rc, info = g.gemm_f16f32_plan(M, N, K, a, b, c, lda or K, ldb or N, ldc or N,
+                                  opts=opts or None)
+    assert rc == g.OK
+    return info
+
+
+def test_plans_for_the_five_workloads():
+    p = plan(512, 512, 512)
+    assert (p["path"], p["bm"], p["bn"], p["num_programs"]) == (g.PATH_ALIGNED, 128, 64, 32)
+    p = plan(1024, 768, 128, tile=g.TILE_128x64x64, group_m=2)
+    assert (p["num_pid_m"], p["num_pid_n"], p["num_programs"], p["group_m"]) == (8, 12, 96, 2)
+    p = plan(4096, 4096, 4096)
+    assert (p["path"], p["bm"], p["bn"], p["num_programs"]) == (g.PATH_ALIGNED, 256, 256, 256)
+    p = plan(8192, 8192, 8192)
+    assert (p["path"], p["bm"], p["bn"], p["num_programs"]) == (g.PATH_ALIGNED, 256, 256, 1024)
+    assert p["xcd_remap"] == 1
+    p = plan(4095, 4097, 4093, group_m=6)
+    assert (p["path"], p["num_pid_m"], p["num_pid_n"], p["num_programs"]) == \
+        (g.PATH_GENERIC, 16, 17, 272)
+
+
+def test_aligned_path_conditions():
+    assert plan(256, 256, 256)["path"] == g.PATH_ALIGNED
+    assert plan(256, 256, 256, force_generic=1)["path"] == g.PATH_GENERIC
+    assert plan(256, 256, 200)["path"] == g.PATH_GENERIC          # K % 64
+    assert plan(256, 250, 256, ldb=256, ldc=256)["path"] == g.PATH_GENERIC  # N % 8
+    assert plan(256, 256, 256, lda=260)["path"] == g.PATH_GENERIC  # lda % 8
+    assert plan(256, 256, 256, a=PA + 2)["path"] == g.PATH_GENERIC  # alignment
+    assert plan(300, 256, 256)["path"] == g.PATH_ALIGNED           # M tail is clamped
+    assert plan(256, 256, 256, xcd_remap=2)["xcd_remap"] == 0

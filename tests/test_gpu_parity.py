@@ -1,0 +1,274 @@
+"""GPU parity: the HIP path, called through the C-ABI, against the CPU oracle.
+
+Full comparison where the oracle finishes in seconds (the 512^3 and 1024x768x128 workloads
+and many small/ragged shapes); at 4096^3, 8192^3 and 4095x4097x4093 sampled elements are
+compared one by one and every row and column of C is checked through checksums.  The
+tolerance is 1e-2 + 2^-10 |oracle| element-wise; results that have one correct value (the
+tile map, closed-form sums exact in fp32, runs that must repeat the same fp32 order) are
+compared bit for bit.
+"""
+import numpy as np
+import pytest
+
+import dense_gemm_f16f32_amd as g
+import oracle
+from gpu_util import assert_within_tolerance, f64, from_dev, to_dev
+from synthetic_inputs import operands, workload
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def run(A_dev, B_dev, M, N, K, C_dev=None, **opts):
+    return g.matmul(A_dev, B_dev, C_dev, M=M, N=N, K=K, **opts)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _sync_after():
+    yield
+    torch.cuda.synchronize()
+
+
+# ---------------------------------------------------------------------------------------
+# Tile map: bit-exact against the oracle's grouped map and XCD permutation.
+# ---------------------------------------------------------------------------------------
+@pytest.mark.parametrize("m,n,G", [(8, 12, 2), (16, 16, 8), (16, 17, 6), (32, 32, 8), (1, 1, 1),
+                                   (3, 7, 5), (40, 33, 7), (5, 3, 3), (64, 64, 4)])
+@pytest.mark.parametrize("remap", [g.REMAP_ON, g.REMAP_OFF])
+def test_tile_map_bit_exact(m, n, G, remap):
+    got = g.tile_map(m, n, G, remap).cpu().numpy().astype(np.int64)
+    want = oracle.program_tiles(m, n, G, remap == g.REMAP_ON)
+    assert np.array_equal(got, want)
+
+
+def test_tile_map_worked_example():
+    """1024x768 with 128x64 tiles and G = 2: 96 programs, program 60 -> (4, 6)."""
+    t = g.tile_map(8, 12, 2, g.REMAP_OFF).cpu().numpy()
+    assert t.shape == (96, 3) and tuple(t[60]) == (60, 4, 6)
+
+
+# ---------------------------------------------------------------------------------------
+# Small workloads: full comparison.
+# ---------------------------------------------------------------------------------------
+def test_workload_512_full():
+    _, M, N, K, dist, seed = workload("gemm512_u")
+    A, B = operands(M, N, K, dist, seed)
+    C = from_dev(run(to_dev(A), to_dev(B), M, N, K))
+    want = oracle.gemm(A, B)
+    assert_within_tolerance(C, want, "512^3")
+    # the tutorial's own check: allclose against torch.matmul with atol 1e-2, rtol 0
+    ref = torch.matmul(to_dev(A).view(torch.float16), to_dev(B).view(torch.float16))
+    got = torch.from_numpy(C.view(np.float16)).cuda()
+    assert torch.allclose(got, ref, atol=1e-2, rtol=0)
+
+
+def test_workload_1024x768x128_grouped_full():
+    _, M, N, K, dist, seed = workload("gemm1024x768x128_u01")
+    A, B = operands(M, N, K, dist, seed)
+    opts = dict(tile=g.TILE_128x64x64, group_m=2)
+    rc, info = g.gemm_f16f32_plan(M, N, K, 1 << 20, 2 << 20, 3 << 20, K, N, N, opts=opts)
+    assert rc == g.OK and (info["num_pid_m"], info["num_pid_n"]) == (8, 12)
+    C = from_dev(run(to_dev(A), to_dev(B), M, N, K, **opts))
+    assert_within_tolerance(C, oracle.gemm(A, B), "1024x768x128")
+    for remap in (g.REMAP_ON, g.REMAP_OFF):
+        got = g.tile_map(8, 12, 2, remap).cpu().numpy().astype(np.int64)
+        assert np.array_equal(got, oracle.program_tiles(8, 12, 2, remap == g.REMAP_ON))
+
+
+# ---------------------------------------------------------------------------------------
+# Full-size workloads: sampled elements and checksums.
+# ---------------------------------------------------------------------------------------
+def sample_positions(M, N, bm, bn, per_tile, seed):
+    """Per output tile: its four corners plus `per_tile` random elements; plus C's corners."""
+    rng = np.random.default_rng(seed)
+    rows, cols = [], []
+    for tm in range(0, M, bm):
+        for tn in range(0, N, bn):
+            r1, c1 = min(tm + bm, M) - 1, min(tn + bn, N) - 1
+            rows += [tm, tm, r1, r1]
+            cols += [tn, c1, tn, c1]
+            rows += list(rng.integers(tm, r1 + 1, per_tile))
+            cols += list(rng.integers(tn, c1 + 1, per_tile))
+    rows += [0, 0, M - 1, M - 1]
+    cols += [0, N - 1, 0, N - 1]
+    return np.array(rows, dtype=np.int64), np.array(cols, dtype=np.int64)
+
+
+def checksum_ok(A, B, C):
+    """Row and column sums of C against A (B 1) and (1^T A) B in fp64.
+
+    Each C element is within 1e-2 + 2^-10 |C| of the exact sum, so a row's total error is
+    within N * 1e-2 + 2^-10 sum|C| (and likewise per column); a wrong or missing tile, a
+    dropped k panel or a misplaced row breaks these by far more.
+    """
+    a, b, c = f64(A), f64(B), f64(C)
+    row_want = a @ b.sum(axis=1)
+    col_want = a.sum(axis=0) @ b
+    row_err = np.abs(c.sum(axis=1) - row_want)
+    col_err = np.abs(c.sum(axis=0) - col_want)
+    row_bound = c.shape[1] * 1e-2 + 2.0 ** -10 * np.abs(c).sum(axis=1)
+    col_bound = c.shape[0] * 1e-2 + 2.0 ** -10 * np.abs(c).sum(axis=0)
+    return bool(np.all(row_err <= row_bound) and np.all(col_err <= col_bound))
+
+
+@pytest.mark.parametrize("name", ["gemm4096_u", "gemm8192_u", "gemm4095x4097x4093_n"])
+def test_large_workload_sampled(name):
+    _, M, N, K, dist, seed = workload(name)
+    A, B = operands(M, N, K, dist, seed)
+    opts = dict(group_m=6) if name.startswith("gemm4095") else {}
+    rc, info = g.gemm_f16f32_plan(M, N, K, 1 << 40, 2 << 40, 3 << 40, K, N, N,
+                                  opts=opts or None)
+    assert rc == g.OK
+    if name.startswith("gemm4095"):
+        # ragged: generic path, 16 x 17 tiles, and G = 6 leaves a last group of 4 rows
+        assert info["path"] == g.PATH_GENERIC and info["num_pid_m"] % 6 == 4
+    C = from_dev(run(to_dev(A), to_dev(B), M, N, K, **opts))
+    assert not np.isnan(f64(C)).any()
+    r, c = sample_positions(M, N, info["bm"], info["bn"], 6, seed)
+    want = oracle.gemm_sampled(A, B, r, c)
+    assert_within_tolerance(C[r, c], want, name)
+    assert checksum_ok(A, B, C), name
+
+
+def test_ragged_equals_zero_padded():
+    """The masked run equals the aligned run on zero-padded operands, bit for bit: zeros add
+    +0 to the same fp32 sums in the same order."""
+    _, M, N, K, dist, seed = workload("gemm4095x4097x4093_n")
+    A, B = operands(M, N, K, dist, seed)
+    Mp, Np, Kp = 4096, 4104, 4096
+    Ap = np.zeros((Mp, Kp), np.uint16)
+    Ap[:M, :K] = A
+    Bp = np.zeros((Kp, Np), np.uint16)
+    Bp[:K, :N] = B
+    opts = dict(tile=g.TILE_256x256x64, group_m=6)
+    C = from_dev(run(to_dev(A), to_dev(B), M, N, K, **opts))
+    rc, info = g.gemm_f16f32_plan(Mp, Np, Kp, 1 << 40, 2 << 40, 3 << 40, Kp, Np, Np, opts=opts)
+    assert info["path"] == g.PATH_ALIGNED
+    Cp = from_dev(run(to_dev(Ap), to_dev(Bp), Mp, Np, Kp, **opts))
+    assert np.array_equal(C, Cp[:M, :N])
+
+
+# ---------------------------------------------------------------------------------------
+# Invariants on one shape: paths, alignment, group size and remap change no bit.
+# ---------------------------------------------------------------------------------------
+@pytest.fixture(scope="module")
+def ops2048():
+    A, B = operands(2048, 2048, 2048, "u(-0.5,0.5)", 7)
+    return A, B, to_dev(A), to_dev(B)
+
+
+def test_generic_path_bitwise_equals_aligned(ops2048):
+    A, B, Ad, Bd = ops2048
+    ref = from_dev(run(Ad, Bd, 2048, 2048, 2048, tile=g.TILE_256x256x64))
+    gen = from_dev(run(Ad, Bd, 2048, 2048, 2048, tile=g.TILE_256x256x64, force_generic=1))
+    assert np.array_equal(ref, gen)
+    # operands starting 2 bytes past an aligned address (odd-offset rows in the generic path)
+    Ab = torch.zeros(2048 * 2048 + 8, dtype=torch.int16, device="cuda")
+    Bb = torch.zeros(2048 * 2048 + 8, dtype=torch.int16, device="cuda")
+    Ab[1:1 + 2048 * 2048] = Ad.reshape(-1)
+    Bb[3:3 + 2048 * 2048] = Bd.reshape(-1)
+    Au = Ab[1:1 + 2048 * 2048].view(2048, 2048)
+    Bu = Bb[3:3 + 2048 * 2048].view(2048, 2048)
+    odd = from_dev(run(Au, Bu, 2048, 2048, 2048, tile=g.TILE_256x256x64))
+    assert np.array_equal(ref, odd)
+
+
+def test_group_and_remap_change_no_bit(ops2048):
+    A, B, Ad, Bd = ops2048
+    ref = from_dev(run(Ad, Bd, 2048, 2048, 2048, tile=g.TILE_256x256x64, group_m=1))
+    for G in (2, 4, 8, 16):
+        for remap in (g.REMAP_ON, g.REMAP_OFF):
+            got = from_dev(run(Ad, Bd, 2048, 2048, 2048, tile=g.TILE_256x256x64, group_m=G,
+                               xcd_remap=remap))
+            assert np.array_equal(ref, got), (G, remap)
+
+
+def test_run_to_run_deterministic(ops2048):
+    A, B, Ad, Bd = ops2048
+    first = from_dev(run(Ad, Bd, 2048, 2048, 2048))
+    for _ in range(3):
+        assert np.array_equal(first, from_dev(run(Ad, Bd, 2048, 2048, 2048)))
+
+
+def test_every_tile_config_within_tolerance(ops2048):
+    A, B, Ad, Bd = ops2048
+    rows, cols = sample_positions(2048, 2048, 128, 128, 4, 1)
+    want = oracle.gemm_sampled(A, B, rows, cols)
+    for tile in g.TILES:
+        for fg in (0, 1):
+            C = from_dev(run(Ad, Bd, 2048, 2048, 2048, tile=tile, force_generic=fg))
+            assert_within_tolerance(C[rows, cols], want, f"tile {tile} generic {fg}")
+
+
+# ---------------------------------------------------------------------------------------
+# Edge shapes against the full oracle, with canaries in the leading-dimension padding.
+# ---------------------------------------------------------------------------------------
+EDGE = [(1, 1, 1), (1, 1, 64), (7, 9, 13), (255, 1, 61), (257, 129, 65), (300, 200, 64),
+        (64, 64, 4096), (33, 8, 64), (129, 65, 127), (511, 513, 190), (2, 300, 1), (256, 256, 64)]
+
+
+@pytest.mark.parametrize("M,N,K", EDGE)
+@pytest.mark.parametrize("tile", sorted(g.TILES))
+def test_edge_shapes_full_oracle(M, N, K, tile):
+    A, B = operands(M, N, K, "n(0,0.1)", M * 7 + N * 3 + K)
+    pad = 3
+    ldc = N + pad
+    Cd = torch.full((M, ldc), 0x5A5A, dtype=torch.int16, device="cuda")
+    run(to_dev(A), to_dev(B), M, N, K, C_dev=Cd, tile=tile)
+    C = from_dev(Cd)
+    assert_within_tolerance(C[:, :N], oracle.gemm(A, B), f"{M}x{N}x{K} tile {tile}")
+    assert np.all(C[:, N:] == 0x5A5A), "wrote into the ldc padding"
+
+
+@pytest.mark.parametrize("lda_pad,ldb_pad", [(1, 0), (0, 1), (5, 3), (8, 8)])
+def test_leading_dimensions(lda_pad, ldb_pad):
+    M, N, K = 300, 264, 192
+    A, B = operands(M, N, K, "u(-0.5,0.5)", 5)
+    Ap = np.full((M, K + lda_pad), 0x7C00, np.uint16)  # +inf in the padding: must not be read
+    Ap[:, :K] = A
+    Bp = np.full((K, N + ldb_pad), 0x7C00, np.uint16)
+    Bp[:, :N] = B
+    C = from_dev(run(to_dev(Ap), to_dev(Bp), M, N, K))
+    assert_within_tolerance(C, oracle.gemm(A, B), f"lda pad {lda_pad}, ldb pad {ldb_pad}")
+
+
+def test_k_zero_writes_positive_zero():
+    Cd = torch.full((5, 7), 0x1234, dtype=torch.int16, device="cuda")
+    Ad = torch.zeros((5, 1), dtype=torch.int16, device="cuda")
+    Bd = torch.zeros((1, 7), dtype=torch.int16, device="cuda")
+    run(Ad, Bd, 5, 7, 0, C_dev=Cd)
+    assert np.all(from_dev(Cd) == 0)
+
+
+# ---------------------------------------------------------------------------------------
+# Closed forms that are exact in fp32, so every correct kernel gives the same bits.
+# ---------------------------------------------------------------------------------------
+@pytest.mark.parametrize("K,want", [(2048, 2048.0), (2051, 2052.0), (4093, 4092.0),
+                                    (4095, 4096.0), (4096, 4096.0)])
+def test_all_ones_round_half_even(K, want):
+    """K ones sum to K exactly in fp32; above 2048 the fp16 spacing is 2 and odd K are ties
+    that round to the even pattern (round toward zero would give K - 1)."""
+    M, N = 256, 264
+    one = np.float16(1.0).view(np.uint16)
+    A = np.full((M, K), one, np.uint16)
+    B = np.full((K, N), one, np.uint16)
+    C = from_dev(run(to_dev(A), to_dev(B), M, N, K))
+    assert np.all(C == np.float16(want).view(np.uint16))
+
+
+def test_identity_gives_b_exactly():
+    K, N = 384, 256
+    A = np.eye(K, dtype=np.float16).view(np.uint16)
+    _, B = operands(1, N, K, "n(0,0.1)", 3)
+    C = from_dev(run(to_dev(A), to_dev(B), K, N, K))
+    assert np.array_equal(C, B)
+
+
+def test_one_hot_last_k_selects_last_row_of_b():
+    M, N, K = 320, 272, 4093
+    A = np.zeros((M, K), np.uint16)
+    A[:, K - 1] = np.float16(1.0).view(np.uint16)
+    _, B = operands(1, N, K, "u(-0.5,0.5)", 9)
+    C = from_dev(run(to_dev(A), to_dev(B), M, N, K))
+    assert np.array_equal(C, np.broadcast_to(B[K - 1], (M, N)))
