@@ -30,6 +30,13 @@ def build(extra=()) -> str:
         raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
     if msgs:
         print("\n".join(msgs))
+    # Every kernel must have its host launch stub; an undefined one means the host pass
+    # dropped a kernel and the library would fail to load.
+    nm = subprocess.run(["nm", "-D", "--undefined-only", tmp], capture_output=True, text=True)
+    missing = [ln.split()[-1] for ln in nm.stdout.splitlines() if "__device_stub__" in ln]
+    if nm.returncode != 0 or missing:
+        os.remove(tmp)
+        raise RuntimeError("undefined kernel stubs in the built library: " + ", ".join(missing))
     os.replace(tmp, SO)
     return SO
 

@@ -26,6 +26,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+#include <utility>
+
 namespace gk {
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
@@ -88,10 +91,35 @@ struct Tile {
   static_assert(A_LD >= 1 && B_LD >= 1, "tile too small for 256 threads");
 };
 
+// The hardware range-checks each dword of a buffer load on its own and returns 0 for a dword
+// that reaches past num_records, even partly.  The extent is therefore rounded up to whole
+// dwords: a matrix whose last element ends 2 bytes into a dword still gets that element.  The
+// 2 extra bytes share a dword (hence a page) with valid data, and they only ever land in
+// slots that are masked (k >= K) or never stored (columns >= N).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  const int64_t lim = 0xFFFFFFFCll;
+  bytes = (bytes + 3) & ~(int64_t)3;
+  const int n = (int)(uint32_t)(bytes < 0 ? 0 : (bytes > lim ? lim : bytes));
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
+}
+
+// 16-byte buffer -> LDS load: lane l's 16 bytes from (resource, voff) land at dst + 16 l.
+// The builtin exists only for the device; in the host pass of this single-source file the
+// call must not appear at all, or the kernels' host launch stubs are not emitted.
+__device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t r, void GK_LDS* dst,
+                                                  uint32_t voff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, voff, 0, 0, 0);
+#endif
+}
+
 // LDS layouts.  A panel: BM rows of 64 halves (8 chunks of 16 B); chunk c of row r is stored
-// at chunk position c ^ swz_a(r).  Eight (and sixteen) consecutive rows read at the same
-// logical chunk then hit distinct bank groups, which is what the MFMA A-operand read does.
-__device__ __forceinline__ int swz_a(int r) { return (r ^ (r >> 3)) & 7; }
+// at chunk position c ^ swz_a(r), with swz_a(r) = (r mod 8) xor bit 3 of r.  Eight
+// consecutive rows read at the same logical chunk then hit 8 distinct chunk positions, and
+// sixteen consecutive rows hit 16 distinct (row parity, chunk position) pairs -- what the
+// MFMA A-operand read does.  The swizzle depends on r mod 16 only, so rows 32 apart (the next
+// 32-row MFMA block) share it and their addresses differ by a constant.
+__device__ __forceinline__ int swz_a(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
 // B panel: 64 rows (k) of BN halves; chunk c of row k sits at c ^ swz_b(k).  A transposing
 // read covers 4 consecutive rows x 2 (16 lanes) or x 4 (32 lanes) consecutive chunks; the
@@ -111,75 +139,160 @@ __device__ __forceinline__ int lds_b(int k, int n) {
 }
 
 // ---------------------------------------------------------------------------------------
-// Compute one staged panel: BK/16 steps of TM x TN MFMAs per wave.
+// MFMA operands of one 16-deep k step for one wave: TM A blocks (32 rows x 16 k) and TN B
+// blocks (16 k x 32 columns), read from a staged panel.
 // ---------------------------------------------------------------------------------------
 template <class T>
-__device__ __forceinline__ void mma_panel(const char GK_LDS* sA, const char GK_LDS* sB,
-                                          float16v (&acc)[T::TM][T::TN], int wm, int wn,
-                                          int lane) {
+struct Frag {
+  half8 a[T::TM];
+  half8 b[T::TN];
+};
+
+// Per-lane LDS byte offsets of a wave's operand reads inside one stage.  A: one per k step
+// (block tm adds 32 rows = tm * 32 * 128 bytes, and the swizzle of a row depends only on
+// row % 16, so that is an immediate).  B: one per 32-column block (k step kk and the second
+// 4-deep read add whole rows, which keep row % 4 and hence the swizzle; also immediates).
+template <class T>
+struct LaneOffsets {
+  int a[T::BK / 16];
+  int b[T::TN];
+};
+
+template <class T>
+__device__ __forceinline__ LaneOffsets<T> lane_offsets(int wm, int wn, int lane) {
+  LaneOffsets<T> o;
+#pragma unroll
+  for (int kk = 0; kk < T::BK / 16; ++kk)
+    o.a[kk] = lds_a<T>(wm * T::WTM + (lane & 31), kk * 2 + (lane >> 5));
+  const int g = lane >> 4, i = lane & 15;
+#pragma unroll
+  for (int tn = 0; tn < T::TN; ++tn)
+    o.b[tn] = T::A_BYTES +
+              lds_b<T>((g >> 1) * 8 + (i >> 2), wn * T::WTN + tn * 32 + (g & 1) * 16 + (i & 3) * 4);
+  return o;
+}
+
+// Reads the operands of k step kk from the stage at `st`.
+template <class T>
+__device__ __forceinline__ void read_frags(Frag<T>& f, const char GK_LDS* st,
+                                           const LaneOffsets<T>& o, int kk) {
+#pragma unroll
+  for (int tm = 0; tm < T::TM; ++tm)
+    f.a[tm] = *(const half8 GK_LDS*)(st + o.a[kk] + tm * 32 * (T::CA * 16));
+#pragma unroll
+  for (int tn = 0; tn < T::TN; ++tn) {
+    const char GK_LDS* pb = st + o.b[tn] + kk * 16 * (T::CB * 16);
+    short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((short4v GK_LDS*)pb);
+    short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((short4v GK_LDS*)(pb + 4 * T::CB * 16));
+    f.b[tn] = __builtin_bit_cast(half8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  }
+}
+
+template <class T>
+__device__ __forceinline__ void mfma_step(float16v (&acc)[T::TM][T::TN], const Frag<T>& f) {
+#pragma unroll
+  for (int tm = 0; tm < T::TM; ++tm)
+#pragma unroll
+    for (int tn = 0; tn < T::TN; ++tn)
+      acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.a[tm], f.b[tn], acc[tm][tn], 0, 0, 0);
+}
+
+// One whole staged panel, operands read just before use (generic path).
+template <class T>
+__device__ __forceinline__ void mma_panel(const char GK_LDS* st, float16v (&acc)[T::TM][T::TN],
+                                          const LaneOffsets<T>& o) {
 #pragma unroll
   for (int kk = 0; kk < T::BK / 16; ++kk) {
-    half8 a[T::TM];
-    half8 b[T::TN];
-#pragma unroll
-    for (int tm = 0; tm < T::TM; ++tm) {
-      const int r = wm * T::WTM + tm * 32 + (lane & 31);
-      const int c = kk * 2 + (lane >> 5);
-      a[tm] = *(const half8 GK_LDS*)(sA + lds_a<T>(r, c));
-    }
-#pragma unroll
-    for (int tn = 0; tn < T::TN; ++tn) {
-      const int g = lane >> 4, i = lane & 15;
-      const int n = wn * T::WTN + tn * 32 + (g & 1) * 16 + (i & 3) * 4;
-      const int k = kk * 16 + (g >> 1) * 8 + (i >> 2);
-      short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (short4v GK_LDS*)(sB + lds_b<T>(k, n)));
-      short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (short4v GK_LDS*)(sB + lds_b<T>(k + 4, n)));
-      b[tn] = __builtin_bit_cast(half8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-    }
-#pragma unroll
-    for (int tm = 0; tm < T::TM; ++tm)
-#pragma unroll
-      for (int tn = 0; tn < T::TN; ++tn)
-        acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[tm], b[tn], acc[tm][tn], 0, 0, 0);
+    Frag<T> f;
+    read_frags<T>(f, st, o, kk);
+    mfma_step<T>(acc, f);
   }
 }
 
 // ---------------------------------------------------------------------------------------
 // Epilogue: narrow once (fp32 -> fp16, round to nearest even) and store the wave's block.
+// Stores go through a buffer resource that ends at C's last element, so rows past M are
+// dropped by the hardware; columns past N (which would land in the ldc padding) are masked.
+// Per lane, one VGPR holds the byte offset of its first element; row steps are scalar
+// offsets and 32-column steps immediates.
 // ---------------------------------------------------------------------------------------
 template <class T>
 __device__ __forceinline__ void store_tile(const Args& p, const float16v (&acc)[T::TM][T::TN],
                                            int m0, int n0, int wm, int wn, int lane) {
-  const bool full = (m0 + T::BM <= p.M) && (n0 + T::BN <= p.N);
+  const int64_t c0 = (int64_t)m0 * p.ldc + n0;
+  const int64_t extC = (int64_t)(p.M - 1) * p.ldc + p.N;
+  const __amdgpu_buffer_rsrc_t rc = make_rsrc(p.C + c0, 2 * (extC - c0));
+  const int col = wn * T::WTN + (lane & 31);
+  const uint32_t vbase =
+      2u * ((uint32_t)(wm * T::WTM + (lane >> 5) * 4) * (uint32_t)p.ldc + (uint32_t)col);
+  const uint32_t ldc2 = 2u * (uint32_t)p.ldc;
+  const int ncols = p.N - n0;   // columns of this tile that exist
 #pragma unroll
-  for (int tm = 0; tm < T::TM; ++tm) {
+  for (int tn = 0; tn < T::TN; ++tn) {
+    if (col + tn * 32 < ncols) {
 #pragma unroll
-    for (int tn = 0; tn < T::TN; ++tn) {
-      const int j = n0 + wn * T::WTN + tn * 32 + (lane & 31);
-      const int ib = m0 + wm * T::WTM + tm * 32 + (lane >> 5) * 4;
+      for (int tm = 0; tm < T::TM; ++tm) {
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int i = ib + (v >> 2) * 8 + (v & 3);
-        const _Float16 h = (_Float16)acc[tm][tn][v];
-        if (full || (i < p.M && j < p.N))
-          p.C[(int64_t)i * p.ldc + j] = __builtin_bit_cast(uint16_t, h);
+        for (int v = 0; v < 16; ++v) {
+          const uint32_t rowstep = (uint32_t)(tm * 32 + (v >> 2) * 8 + (v & 3)) * ldc2;
+          const _Float16 h = (_Float16)acc[tm][tn][v];
+          __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, h), rc,
+                                                vbase + tn * 64, rowstep, 0);
+        }
       }
     }
   }
 }
 
+// Wait for this wave's LDS accesses, then meet the other waves.  Written as one asm block so
+// that no LDS access is moved across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // ---------------------------------------------------------------------------------------
-// Aligned path: A and B 16-byte aligned, lda % 8 == 0, ldb % 8 == 0, N % 8 == 0, K % 64 == 0.
-// Each thread issues A_LD + B_LD direct global->LDS 16-byte loads per panel.  Rows past M
-// and column chunks past N are clamped to the last valid ones (their results are never
-// stored), so every load stays inside the caller's matrices.
+// Instruction interleaving inside one k step (one scheduling region): NM MFMAs, with ND LDS
+// reads and NV global loads spread evenly between them.
+// ---------------------------------------------------------------------------------------
+template <int MASK, int COUNT>
+__device__ __forceinline__ void sched_group() {
+  if constexpr (COUNT > 0) __builtin_amdgcn_sched_group_barrier(MASK, COUNT, 0);
+}
+
+template <int NM, int ND, int NV, int... I>
+__device__ __forceinline__ void sched_step(std::integer_sequence<int, I...>) {
+  ((sched_group<0x008, 1>(), sched_group<0x100, (I + 1) * ND / NM - I * ND / NM>(),
+    sched_group<0x020, (I + 1) * NV / NM - I * NV / NM>()),
+   ...);
+}
+
+template <int NM, int ND, int NV>
+__device__ __forceinline__ void sched_step() {
+  sched_step<NM, ND, NV>(std::make_integer_sequence<int, NM>{});
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// ---------------------------------------------------------------------------------------
+// Aligned path: A and B 16-byte aligned, lda % 8 == 0, ldb % 8 == 0, K % 64 == 0.  Each
+// thread issues A_LD + B_LD 16-byte buffer->LDS loads per panel; the buffer resources end at
+// the matrices' last elements, so nothing past them is ever read.
+//
+// Pipeline (per wave): the operands of k step kk+1 are read from LDS while the MFMAs of
+// step kk run.  The one barrier per panel sits in the last k step, after that step's
+// operands are in registers: past it, the stage just consumed is refilled with panel s+2
+// and the first operands of panel s+1 are read from the other stage.  The two stages are
+// separate LDS objects and the loop is unrolled by two, so the compiler can see that the
+// refill never aliases the stage being read and does not wait for it.
 // ---------------------------------------------------------------------------------------
 template <int BM, int BN>
 __global__ void __launch_bounds__(kThreads) gemm_aligned(Args p) {
   using T = Tile<BM, BN>;
-  __shared__ __attribute__((aligned(16))) char smem[2 * T::STAGE];
+  static_assert(T::BK == 64, "the k-step schedule below is written for four 16-deep steps");
+  constexpr int NM = T::TM * T::TN;        // MFMAs per k step
+  constexpr int ND = T::TM + 2 * T::TN;    // LDS reads per k step
+  constexpr int NV = T::A_LD + T::B_LD;    // global->LDS loads per panel
+  __shared__ __attribute__((aligned(16))) char stage0[T::STAGE];
+  __shared__ __attribute__((aligned(16))) char stage1[T::STAGE];
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -190,40 +303,43 @@ __global__ void __launch_bounds__(kThreads) gemm_aligned(Args p) {
                pid, pid_m, pid_n);
   const int m0 = pid_m * BM, n0 = pid_n * BN;
 
-  // Per-thread element offsets of its load slots, relative to the panel's corner.
-  int32_t offA[T::A_LD], offB[T::B_LD];
+  // Per-thread byte offsets of its load slots, relative to the panel's corner.  Rows past M
+  // fall outside the buffer resource and read as zeros; columns past N read whatever lies
+  // there and only feed results that are never stored.
+  uint32_t offA[T::A_LD], offB[T::B_LD];
 #pragma unroll
   for (int i = 0; i < T::A_LD; ++i) {
     const int q = (i * 4 + w) * 64 + lane;
     const int r = q / T::CA, c = (q % T::CA) ^ swz_a(r);
-    const int row = min(m0 + r, p.M - 1) - m0;
-    offA[i] = row * (int32_t)p.lda + c * 8;
+    offA[i] = 2u * ((uint32_t)r * (uint32_t)p.lda + (uint32_t)(c * 8));
   }
 #pragma unroll
   for (int i = 0; i < T::B_LD; ++i) {
     const int q = (i * 4 + w) * 64 + lane;
     const int k = q / T::CB, c = (q % T::CB) ^ swz_b<T::CB>(k);
-    const int col = min(n0 + c * 8, p.N - 8) - n0;
-    offB[i] = k * (int32_t)p.ldb + col;
+    offB[i] = 2u * ((uint32_t)k * (uint32_t)p.ldb + (uint32_t)(c * 8));
   }
 
-  const uint16_t* gA = p.A + (int64_t)m0 * p.lda;
-  const uint16_t* gB = p.B + n0;
+  // Extents (elements from each matrix's first element to one past its last).
+  const int64_t extA = (int64_t)(p.M - 1) * p.lda + p.K;
+  const int64_t extB = (int64_t)(p.K - 1) * p.ldb + p.N;
   const int nk = p.K / T::BK;
 
-  auto issue = [&](int s, int stage) {
-    const uint16_t* pa = gA + s * T::BK;
-    const uint16_t* pb = gB + (int64_t)s * T::BK * p.ldb;
-    char GK_LDS* base = (char GK_LDS*)smem + stage * T::STAGE;
+  // Panel s of A starts at A[m0][64 s], of B at B[64 s][n0]; each gets a buffer resource
+  // (scalar registers) that ends at its matrix's last element.  A panel index s >= nk gets an
+  // empty resource: its loads touch no memory and deposit zeros.
+  auto issue = [&](int s, char GK_LDS* base) __attribute__((always_inline)) {
+    const bool live = s < nk;
+    const int64_t a0 = (int64_t)m0 * p.lda + (int64_t)s * T::BK;
+    const int64_t b0 = (int64_t)s * T::BK * p.ldb + n0;
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.A + (live ? a0 : 0), live ? 2 * (extA - a0) : 0);
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.B + (live ? b0 : 0), live ? 2 * (extB - b0) : 0);
 #pragma unroll
     for (int i = 0; i < T::A_LD; ++i)
-      __builtin_amdgcn_global_load_lds((const void*)(pa + offA[i]),
-                                       (void GK_LDS*)(base + (i * 4 + w) * 1024), 16, 0, 0);
+      buffer_load_lds16(ra, (void GK_LDS*)(base + (i * 4 + w) * 1024), offA[i]);
 #pragma unroll
     for (int i = 0; i < T::B_LD; ++i)
-      __builtin_amdgcn_global_load_lds((const void*)(pb + offB[i]),
-                                       (void GK_LDS*)(base + T::A_BYTES + (i * 4 + w) * 1024),
-                                       16, 0, 0);
+      buffer_load_lds16(rb, (void GK_LDS*)(base + T::A_BYTES + (i * 4 + w) * 1024), offB[i]);
   };
 
   float16v acc[T::TM][T::TN];
@@ -233,16 +349,55 @@ __global__ void __launch_bounds__(kThreads) gemm_aligned(Args p) {
     for (int tn = 0; tn < T::TN; ++tn)
       acc[tm][tn] = float16v{};
 
-  if (nk > 0) issue(0, 0);
-  for (int s = 0; s < nk; ++s) {
-    // Own loads of panel s have landed; after the barrier every wave's have, and every wave
-    // has finished reading the other stage (panel s-1).
+  char GK_LDS* const S0 = (char GK_LDS*)stage0;
+  char GK_LDS* const S1 = (char GK_LDS*)stage1;
+  const LaneOffsets<T> lo = lane_offsets<T>(wm, wn, lane);
+  Frag<T> f0, f1;
+
+  // One panel from stage `cur`, with panel s+1 in `nxt`.  After the barrier in the last k
+  // step `cur` is refilled with panel s+2 and the first operands of panel s+1 are read.
+  auto panel = [&](int s, char GK_LDS* cur, char GK_LDS* nxt) __attribute__((always_inline)) {
+    read_frags<T>(f1, cur, lo, 1);
+    mfma_step<T>(acc, f0);
+    sched_step<NM, ND, 0>();
+    read_frags<T>(f0, cur, lo, 2);
+    mfma_step<T>(acc, f1);
+    sched_step<NM, ND, 0>();
+    read_frags<T>(f1, cur, lo, 3);
+    mfma_step<T>(acc, f0);
+    sched_step<NM, ND, 0>();
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (s + 1 < nk) issue(s + 1, (s + 1) & 1);
-    const char GK_LDS* base = (const char GK_LDS*)smem + (s & 1) * T::STAGE;
-    mma_panel<T>(base, base + T::A_BYTES, acc, wm, wn, lane);
+    lds_barrier();
+    issue(s + 2, cur);
+    read_frags<T>(f0, nxt, lo, 0);
+    mfma_step<T>(acc, f1);
+    sched_step<NM, ND, NV>();
+  };
+
+  // Panels run in pairs (stage 0, then stage 1) with no branch inside a pair.  An odd panel
+  // count is padded with one all-zero panel, which adds exactly +0 to every accumulator.
+  if (nk > 0) {
+    issue(0, S0);
+    issue(1, S1);
+    if constexpr (NV == 16)
+      asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+    else if constexpr (NV == 12)
+      asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
+    else if constexpr (NV == 8)
+      asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    else if constexpr (NV == 6)
+      asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    lds_barrier();
+    read_frags<T>(f0, S0, lo, 0);
   }
+  for (int s = 0; s < nk; s += 2) {
+    panel(s, S0, S1);
+    panel(s + 1, S1, S0);
+  }
+  // The last refills (of panels past the end) must land before the workgroup's LDS is freed.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   store_tile<T>(p, acc, m0, n0, wm, wn, lane);
 }
 
@@ -253,12 +408,6 @@ __global__ void __launch_bounds__(kThreads) gemm_aligned(Args p) {
 // some row starts are only 2-byte aligned, so each 16-byte chunk is assembled from a
 // 4-byte-aligned dwordx4 plus one more dword and a byte funnel shift.
 // ---------------------------------------------------------------------------------------
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
-  const int64_t lim = 0xFFFFFFFFll;
-  const int n = (int)(uint32_t)(bytes < 0 ? 0 : (bytes > lim ? lim : bytes));
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
-}
-
 template <bool kOdd>
 __device__ __forceinline__ u32x4 load_chunk(__amdgpu_buffer_rsrc_t rs, uint32_t off_bytes) {
   if (!kOdd) {
@@ -349,6 +498,7 @@ __global__ void __launch_bounds__(kThreads) gemm_generic(Args p) {
     }
   };
 
+  const LaneOffsets<T> lo = lane_offsets<T>(wm, wn, lane);
   float16v acc[T::TM][T::TN];
 #pragma unroll
   for (int tm = 0; tm < T::TM; ++tm)
@@ -363,8 +513,7 @@ __global__ void __launch_bounds__(kThreads) gemm_generic(Args p) {
   for (int s = 0; s < nk; ++s) {
     __syncthreads();
     if (s + 1 < nk) fetch(s + 1);
-    const char GK_LDS* base = (const char GK_LDS*)smem + (s & 1) * T::STAGE;
-    mma_panel<T>(base, base + T::A_BYTES, acc, wm, wn, lane);
+    mma_panel<T>((const char GK_LDS*)smem + (s & 1) * T::STAGE, acc, lo);
     if (s + 1 < nk) deposit((s + 1) & 1);
   }
   store_tile<T>(p, acc, m0, n0, wm, wn, lane);
