@@ -56,16 +56,29 @@ def measured_traffic(workload: str, tile: int, group_m: int, remap: int):
     return e.get("bytes_per_launch")
 
 
-def time_workload(g, torch, name, steps, warmup, opts):
+_DEVICE_OPERANDS = {}
+
+
+def device_operands(torch, name):
+    """(A, B, C) device tensors of a workload, generated once per process."""
     import numpy as np
     from synthetic_inputs import operands, workload
 
-    _, M, N, K, dist, seed = workload(name)
-    A, B = operands(M, N, K, dist, seed)
-    Ad = torch.from_numpy(A.view(np.int16)).cuda()
-    Bd = torch.from_numpy(B.view(np.int16)).cuda()
-    Cd = torch.empty((M, N), dtype=torch.int16, device="cuda")
-    del A, B
+    if name not in _DEVICE_OPERANDS:
+        _DEVICE_OPERANDS.clear()
+        _, M, N, K, dist, seed = workload(name)
+        A, B = operands(M, N, K, dist, seed)
+        _DEVICE_OPERANDS[name] = (torch.from_numpy(A.view(np.int16)).cuda(),
+                                  torch.from_numpy(B.view(np.int16)).cuda(),
+                                  torch.empty((M, N), dtype=torch.int16, device="cuda"))
+    return _DEVICE_OPERANDS[name]
+
+
+def time_workload(g, torch, name, steps, warmup, opts):
+    from synthetic_inputs import workload
+
+    _, M, N, K, _, _ = workload(name)
+    Ad, Bd, Cd = device_operands(torch, name)
     rc, plan = g.gemm_f16f32_plan(M, N, K, Ad.data_ptr(), Bd.data_ptr(), Cd.data_ptr(), K, N, N,
                                   opts=opts or None)
     if rc != g.OK:
@@ -94,6 +107,46 @@ def time_workload(g, torch, name, steps, warmup, opts):
         "kernel_ms_min": per[0], "kernel_ms_p90": per[min(len(per) - 1, int(0.9 * len(per)))],
         "achieved_tflops": flops / (mean_ms * 1e-3) / 1e12,
     }
+
+
+def time_torch(torch, name, steps, warmup):
+    """torch.matmul (the vendor BLAS) on the same fp16 operands, for context only."""
+    from synthetic_inputs import workload
+
+    _, M, N, K, _, _ = workload(name)
+    Ad, Bd, _ = device_operands(torch, name)
+    a, b = Ad.view(torch.float16), Bd.view(torch.float16)
+    for _ in range(warmup):
+        torch.matmul(a, b)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for s, e in ev:
+        s.record()
+        torch.matmul(a, b)
+        e.record()
+    torch.cuda.synchronize()
+    per = sorted(s.elapsed_time(e) for s, e in ev)
+    mean = sum(per) / len(per)
+    return {"context": "torch.matmul", "workload": name,
+            "tflops": round(2.0 * M * N * K / (mean * 1e-3) / 1e12, 1),
+            "kernel_ms_median": round(per[len(per) // 2], 4)}
+
+
+def copy_calibration(torch, mib, steps):
+    """A plain device copy of known size, timed; profiled with the same HBM counters as the
+    GEMM it gives the factor between counter readings and bytes actually moved."""
+    n = mib * (1 << 20)
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / steps
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "steps": steps,
+                      "GB_per_s": round(2 * n / dt / 1e9, 1)}), flush=True)
 
 
 def cpu_baseline(name: str, rows: int = 256):
@@ -128,6 +181,12 @@ def main():
     ap.add_argument("--xcd-remap", type=int, default=0)
     ap.add_argument("--force-generic", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sweep", action="store_true",
+                    help="time GROUP_SIZE_M in 1..32 with the XCD permutation on and off (stderr)")
+    ap.add_argument("--torch", action="store_true",
+                    help="also time torch.matmul on the same operands (stderr, context only)")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="only time a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -140,6 +199,9 @@ def main():
     from synthetic_inputs import WORKLOADS
 
     torch.cuda.set_device(0)
+    if args.copy_mib:
+        copy_calibration(torch, args.copy_mib, args.steps)
+        return
     opts = {k: v for k, v in (("tile", args.tile), ("group_m", args.group_m),
                               ("xcd_remap", args.xcd_remap),
                               ("force_generic", args.force_generic)) if v}
@@ -150,6 +212,20 @@ def main():
             r = time_workload(g, torch, w[0], 1000 if small else 50, 10, opts)
             r["frac_of_peak"] = r["achieved_tflops"] / PEAK_TFLOPS
             print(json.dumps(r), file=sys.stderr, flush=True)
+
+    if args.sweep:
+        for G in (1, 2, 4, 8, 16, 32):
+            for remap in (1, 2):
+                o = dict(opts, group_m=G, xcd_remap=remap)
+                rr = time_workload(g, torch, args.workload, args.steps, args.warmup, o)
+                print(json.dumps({"workload": args.workload, "group_m": G,
+                                  "xcd_remap": remap == 1,
+                                  "tflops": round(rr["achieved_tflops"], 1),
+                                  "kernel_ms_median": round(rr["kernel_ms_median"], 4)}),
+                      file=sys.stderr, flush=True)
+    if args.torch:
+        print(json.dumps(time_torch(torch, args.workload, args.steps, args.warmup)),
+              file=sys.stderr, flush=True)
 
     r = time_workload(g, torch, args.workload, args.steps, args.warmup, opts)
     plan = r["plan"]

@@ -19,9 +19,10 @@ LIB_PATH = os.path.join(PKG, "libgemm_f16f32.so")
 
 OK = 0
 ERR_DIM, ERR_NULL, ERR_LD, ERR_OVERLAP, ERR_OPTS, ERR_TOO_LARGE, ERR_HIP = range(-1, -8, -1)
-TILE_AUTO, TILE_256x256x64, TILE_128x128x64, TILE_128x64x64, TILE_256x128x64 = range(5)
+(TILE_AUTO, TILE_256x256x64, TILE_128x128x64, TILE_128x64x64, TILE_256x128x64,
+ TILE_256x256x32) = range(6)
 TILES = {TILE_256x256x64: (256, 256), TILE_128x128x64: (128, 128), TILE_128x64x64: (128, 64),
-         TILE_256x128x64: (256, 128)}
+         TILE_256x128x64: (256, 128), TILE_256x256x32: (256, 256)}
 PATH_ALIGNED, PATH_GENERIC = 0, 1
 REMAP_DEFAULT, REMAP_ON, REMAP_OFF = 0, 1, 2
 

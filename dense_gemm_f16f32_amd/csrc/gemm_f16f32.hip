@@ -11,15 +11,18 @@ namespace {
 
 constexpr int kVersion = 100;  // 0.1.0
 
+// bk: panel depth of the aligned kernel (the generic kernel always uses 64-deep panels);
+// stages: LDS stages of the aligned kernel.
 struct TileDesc {
-  int id, bm, bn, default_group;
+  int id, bm, bn, bk, stages, default_group;
 };
 
 constexpr TileDesc kTiles[] = {
-    {GEMM_F16F32_TILE_256x256x64, 256, 256, 8},
-    {GEMM_F16F32_TILE_128x128x64, 128, 128, 4},
-    {GEMM_F16F32_TILE_128x64x64, 128, 64, 4},
-    {GEMM_F16F32_TILE_256x128x64, 256, 128, 8},
+    {GEMM_F16F32_TILE_256x256x64, 256, 256, 64, 2, 8},
+    {GEMM_F16F32_TILE_128x128x64, 128, 128, 64, 2, 4},
+    {GEMM_F16F32_TILE_128x64x64, 128, 64, 64, 2, 4},
+    {GEMM_F16F32_TILE_256x128x64, 256, 128, 64, 2, 8},
+    {GEMM_F16F32_TILE_256x256x32, 256, 256, 32, 4, 8},
 };
 
 const TileDesc* find_tile(int id) {
@@ -82,13 +85,13 @@ int plan(int64_t M, int64_t N, int64_t K, const uint16_t* A, const uint16_t* B,
   if ((int64_t)t->bm * lda >= kMax || (int64_t)gk::kBK * ldb >= kMax) return GEMM_F16F32_ERR_TOO_LARGE;
 
   const bool aligned = !o.force_generic && ((uintptr_t)A % 16 == 0) && ((uintptr_t)B % 16 == 0) &&
-                       lda % 8 == 0 && ldb % 8 == 0 && N % 8 == 0 && K % gk::kBK == 0;
+                       lda % 8 == 0 && ldb % 8 == 0 && K % t->bk == 0;
   gemm_f16f32_plan_info r;
   r.path = aligned ? GEMM_F16F32_PATH_ALIGNED : GEMM_F16F32_PATH_GENERIC;
   r.tile = t->id;
   r.bm = t->bm;
   r.bn = t->bn;
-  r.bk = gk::kBK;
+  r.bk = aligned ? t->bk : gk::kBK;
   r.group_m = o.group_m ? o.group_m : t->default_group;
   r.xcd_remap = (o.xcd_remap == 2) ? 0 : 1;
   r.num_pid_m = emptyC ? 0 : (int32_t)cdiv(M, t->bm);
@@ -100,12 +103,12 @@ int plan(int64_t M, int64_t N, int64_t K, const uint16_t* A, const uint16_t* B,
   return GEMM_F16F32_OK;
 }
 
-template <int BM, int BN>
+template <int BM, int BN, int BK, int NS>
 hipError_t launch(const gemm_f16f32_plan_info& r, const gk::Args& a, bool odd,
                   hipStream_t stream) {
   const dim3 grid(r.num_programs), block(gk::kThreads);
   if (r.path == GEMM_F16F32_PATH_ALIGNED)
-    hipLaunchKernelGGL((gk::gemm_aligned<BM, BN>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((gk::gemm_aligned<BM, BN, BK, NS>), grid, block, 0, stream, a);
   else if (odd)
     hipLaunchKernelGGL((gk::gemm_generic<BM, BN, true>), grid, block, 0, stream, a);
   else
@@ -151,10 +154,11 @@ int gemm_f16f32_ex(int64_t M, int64_t N, int64_t K, const uint16_t* A, const uin
 
   hipError_t e = hipSuccess;
   switch (r.tile) {
-    case GEMM_F16F32_TILE_256x256x64: e = launch<256, 256>(r, a, odd, s); break;
-    case GEMM_F16F32_TILE_256x128x64: e = launch<256, 128>(r, a, odd, s); break;
-    case GEMM_F16F32_TILE_128x128x64: e = launch<128, 128>(r, a, odd, s); break;
-    case GEMM_F16F32_TILE_128x64x64: e = launch<128, 64>(r, a, odd, s); break;
+    case GEMM_F16F32_TILE_256x256x64: e = launch<256, 256, 64, 2>(r, a, odd, s); break;
+    case GEMM_F16F32_TILE_256x128x64: e = launch<256, 128, 64, 2>(r, a, odd, s); break;
+    case GEMM_F16F32_TILE_128x128x64: e = launch<128, 128, 64, 2>(r, a, odd, s); break;
+    case GEMM_F16F32_TILE_128x64x64: e = launch<128, 64, 64, 2>(r, a, odd, s); break;
+    case GEMM_F16F32_TILE_256x256x32: e = launch<256, 256, 32, 4>(r, a, odd, s); break;
     default: return GEMM_F16F32_ERR_OPTS;
   }
   return e == hipSuccess ? GEMM_F16F32_OK : GEMM_F16F32_ERR_HIP;

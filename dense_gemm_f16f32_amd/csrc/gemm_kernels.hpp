@@ -75,9 +75,9 @@ __device__ __forceinline__ void program_tile(int h, int P, int num_pid_m, int nu
 // ---------------------------------------------------------------------------------------
 // Tile geometry.
 // ---------------------------------------------------------------------------------------
-template <int BM_, int BN_>
+template <int BM_, int BN_, int BK_ = kBK>
 struct Tile {
-  static constexpr int BM = BM_, BN = BN_, BK = kBK;
+  static constexpr int BM = BM_, BN = BN_, BK = BK_;
   static constexpr int WTM = BM / 2, WTN = BN / 2;   // per-wave block of C
   static constexpr int TM = WTM / 32, TN = WTN / 32; // 32x32 MFMA blocks per wave
   static constexpr int CA = BK / 8;                  // 16-byte chunks per LDS row of A
@@ -87,7 +87,7 @@ struct Tile {
   static constexpr int STAGE = A_BYTES + B_BYTES;
   static constexpr int A_LD = A_BYTES / (kThreads * 16);  // 16-byte loads per thread
   static constexpr int B_LD = B_BYTES / (kThreads * 16);
-  static_assert(TM >= 1 && TN >= 1 && CA == 8, "tile shape");
+  static_assert(TM >= 1 && TN >= 1 && (CA == 8 || CA == 4), "tile shape");
   static_assert(A_LD >= 1 && B_LD >= 1, "tile too small for 256 threads");
 };
 
@@ -97,10 +97,12 @@ struct Tile {
 // 2 extra bytes share a dword (hence a page) with valid data, and they only ever land in
 // slots that are masked (k >= K) or never stored (columns >= N).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
-  const int64_t lim = 0xFFFFFFFCll;
-  bytes = (bytes + 3) & ~(int64_t)3;
-  const int n = (int)(uint32_t)(bytes < 0 ? 0 : (bytes > lim ? lim : bytes));
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
+  // Saturate to [0, 2^32 - 4] with 32-bit scalar operations only (no 64-bit compares, which
+  // the scalar unit lacks and would move to the vector unit).
+  const uint64_t b = (uint64_t)(bytes + 3) & ~(uint64_t)3;
+  const uint32_t hi = (uint32_t)(b >> 32), lo = (uint32_t)b;
+  const uint32_t n = (hi & 0x80000000u) ? 0u : (hi ? 0xFFFFFFFCu : lo);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)n, 0x00020000);
 }
 
 // 16-byte buffer -> LDS load: lane l's 16 bytes from (resource, voff) land at dst + 16 l.
@@ -113,15 +115,26 @@ __device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t r, void
 #endif
 }
 
-// LDS layouts.  A panel: BM rows of 64 halves (8 chunks of 16 B); chunk c of row r is stored
-// at chunk position c ^ swz_a(r), with swz_a(r) = (r mod 8) xor bit 3 of r.  Eight
-// consecutive rows read at the same logical chunk then hit 8 distinct chunk positions, and
-// sixteen consecutive rows hit 16 distinct (row parity, chunk position) pairs -- what the
-// MFMA A-operand read does.  The swizzle depends on r mod 16 only, so rows 32 apart (the next
-// 32-row MFMA block) share it and their addresses differ by a constant.
-__device__ __forceinline__ int swz_a(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+// LDS layouts.  A panel: BM rows of BK halves (CA = BK/8 chunks of 16 B); chunk c of row r is
+// stored at chunk position c ^ swz_a(r).  An MFMA A-operand read has 32 lanes on 32
+// consecutive rows at one logical chunk; the hardware serves such a read 8 lanes (128 B) or
+// 16 lanes (256 B) at a time, so any 8 (and any 16) consecutive rows must land on distinct
+// bank groups:
+//  * 128-byte rows (BK = 64): swz = (r mod 8) xor bit 3 of r -- 8 rows give 8 distinct chunk
+//    positions, 16 rows 16 distinct (row parity, position) pairs;
+//  * 64-byte rows (BK = 32): two rows share a bank line; swz = (bits 1-2 of r) xor (bits 3-4)
+//    gives distinct (r mod 2, position) over 8 rows and distinct (r mod 4, position) over 16.
+// Both depend on r mod 32 only, so rows 32 apart (the next 32-row MFMA block) share the
+// swizzle and their addresses differ by a constant.
+template <int CA>
+__device__ __forceinline__ int swz_a(int r) {
+  if constexpr (CA == 8)
+    return (r & 7) ^ ((r >> 3) & 1);
+  else
+    return ((r >> 1) ^ (r >> 3)) & 3;
+}
 
-// B panel: 64 rows (k) of BN halves; chunk c of row k sits at c ^ swz_b(k).  A transposing
+// B panel: BK rows (k) of BN halves; chunk c of row k sits at c ^ swz_b(k).  A transposing
 // read covers 4 consecutive rows x 2 (16 lanes) or x 4 (32 lanes) consecutive chunks; the
 // XOR values 0, 10, 4, 14 for k % 4 = 0..3 spread both footprints over distinct banks.
 template <int CB>
@@ -131,7 +144,7 @@ __device__ __forceinline__ int swz_b(int k) {
 
 template <class T>
 __device__ __forceinline__ int lds_a(int r, int c) {
-  return r * (T::CA * 16) + ((c ^ swz_a(r)) << 4);
+  return r * (T::CA * 16) + ((c ^ swz_a<T::CA>(r)) << 4);
 }
 template <class T>
 __device__ __forceinline__ int lds_b(int k, int n) {
@@ -149,8 +162,7 @@ struct Frag {
 };
 
 // Per-lane LDS byte offsets of a wave's operand reads inside one stage.  A: one per k step
-// (block tm adds 32 rows = tm * 32 * 128 bytes, and the swizzle of a row depends only on
-// row % 16, so that is an immediate).  B: one per 32-column block (k step kk and the second
+// (block tm adds 32 rows, which keep the swizzle, so that is an immediate).  B: one per 32-column block (k step kk and the second
 // 4-deep read add whole rows, which keep row % 4 and hence the swizzle; also immediates).
 template <class T>
 struct LaneOffsets {
@@ -272,27 +284,41 @@ __device__ __forceinline__ void sched_step() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
+// s_waitcnt vmcnt(N) for a compile-time N: wait until at most N vector-memory loads of this
+// wave are outstanding (loads complete in issue order).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N <= 63, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
 // ---------------------------------------------------------------------------------------
-// Aligned path: A and B 16-byte aligned, lda % 8 == 0, ldb % 8 == 0, K % 64 == 0.  Each
+// Aligned path: A and B 16-byte aligned, lda % 8 == 0, ldb % 8 == 0, K % BK == 0.  Each
 // thread issues A_LD + B_LD 16-byte buffer->LDS loads per panel; the buffer resources end at
 // the matrices' last elements, so nothing past them is ever read.
 //
-// Pipeline (per wave): the operands of k step kk+1 are read from LDS while the MFMAs of
-// step kk run.  The one barrier per panel sits in the last k step, after that step's
-// operands are in registers: past it, the stage just consumed is refilled with panel s+2
-// and the first operands of panel s+1 are read from the other stage.  The two stages are
-// separate LDS objects and the loop is unrolled by two, so the compiler can see that the
-// refill never aliases the stage being read and does not wait for it.
+// Pipeline (per wave), NS LDS stages, panel s in stage s mod NS: the operands of k step kk+1
+// are read from LDS while the MFMAs of step kk run.  The one barrier per panel sits in the
+// last k step, after that step's operands are in registers; past it the first operands of
+// panel s+1 are read.  Stage refills: see `panel` below.  The stages are separate LDS objects and the loop
+// is unrolled by NS, so the compiler can see that a refill never aliases the stage being read
+// and does not wait for it.  Panels past the end get empty buffer resources: they load zeros,
+// touch no memory and add exactly +0, which keeps the loop free of branches.
 // ---------------------------------------------------------------------------------------
-template <int BM, int BN>
+template <int BM, int BN, int BK, int NS>
 __global__ void __launch_bounds__(kThreads) gemm_aligned(Args p) {
-  using T = Tile<BM, BN>;
-  static_assert(T::BK == 64, "the k-step schedule below is written for four 16-deep steps");
+  using T = Tile<BM, BN, BK>;
+  constexpr int KS = BK / 16;              // k steps per panel
   constexpr int NM = T::TM * T::TN;        // MFMAs per k step
   constexpr int ND = T::TM + 2 * T::TN;    // LDS reads per k step
-  constexpr int NV = T::A_LD + T::B_LD;    // global->LDS loads per panel
+  constexpr int NV = T::A_LD + T::B_LD;    // buffer->LDS loads per panel
+  static_assert(KS % 2 == 0 && NS >= 2 && NS <= 5, "pipeline shape");
+  static_assert(NS * T::STAGE <= 160 * 1024, "LDS");
   __shared__ __attribute__((aligned(16))) char stage0[T::STAGE];
   __shared__ __attribute__((aligned(16))) char stage1[T::STAGE];
+  __shared__ __attribute__((aligned(16))) char stage2[NS > 2 ? T::STAGE : 16];
+  __shared__ __attribute__((aligned(16))) char stage3[NS > 3 ? T::STAGE : 16];
+  __shared__ __attribute__((aligned(16))) char stage4[NS > 4 ? T::STAGE : 16];
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -310,7 +336,7 @@ __global__ void __launch_bounds__(kThreads) gemm_aligned(Args p) {
 #pragma unroll
   for (int i = 0; i < T::A_LD; ++i) {
     const int q = (i * 4 + w) * 64 + lane;
-    const int r = q / T::CA, c = (q % T::CA) ^ swz_a(r);
+    const int r = q / T::CA, c = (q % T::CA) ^ swz_a<T::CA>(r);
     offA[i] = 2u * ((uint32_t)r * (uint32_t)p.lda + (uint32_t)(c * 8));
   }
 #pragma unroll
@@ -323,15 +349,15 @@ __global__ void __launch_bounds__(kThreads) gemm_aligned(Args p) {
   // Extents (elements from each matrix's first element to one past its last).
   const int64_t extA = (int64_t)(p.M - 1) * p.lda + p.K;
   const int64_t extB = (int64_t)(p.K - 1) * p.ldb + p.N;
-  const int nk = p.K / T::BK;
+  const int nk = p.K / BK;
 
-  // Panel s of A starts at A[m0][64 s], of B at B[64 s][n0]; each gets a buffer resource
+  // Panel s of A starts at A[m0][BK s], of B at B[BK s][n0]; each gets a buffer resource
   // (scalar registers) that ends at its matrix's last element.  A panel index s >= nk gets an
   // empty resource: its loads touch no memory and deposit zeros.
   auto issue = [&](int s, char GK_LDS* base) __attribute__((always_inline)) {
     const bool live = s < nk;
-    const int64_t a0 = (int64_t)m0 * p.lda + (int64_t)s * T::BK;
-    const int64_t b0 = (int64_t)s * T::BK * p.ldb + n0;
+    const int64_t a0 = (int64_t)m0 * p.lda + (int64_t)s * BK;
+    const int64_t b0 = (int64_t)s * BK * p.ldb + n0;
     const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.A + (live ? a0 : 0), live ? 2 * (extA - a0) : 0);
     const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.B + (live ? b0 : 0), live ? 2 * (extB - b0) : 0);
 #pragma unroll
@@ -349,55 +375,60 @@ __global__ void __launch_bounds__(kThreads) gemm_aligned(Args p) {
     for (int tn = 0; tn < T::TN; ++tn)
       acc[tm][tn] = float16v{};
 
-  char GK_LDS* const S0 = (char GK_LDS*)stage0;
-  char GK_LDS* const S1 = (char GK_LDS*)stage1;
+  char GK_LDS* const S[5] = {(char GK_LDS*)stage0, (char GK_LDS*)stage1, (char GK_LDS*)stage2,
+                             (char GK_LDS*)stage3, (char GK_LDS*)stage4};
   const LaneOffsets<T> lo = lane_offsets<T>(wm, wn, lane);
-  Frag<T> f0, f1;
+  Frag<T> f[2];
 
-  // One panel from stage `cur`, with panel s+1 in `nxt`.  After the barrier in the last k
-  // step `cur` is refilled with panel s+2 and the first operands of panel s+1 are read.
-  auto panel = [&](int s, char GK_LDS* cur, char GK_LDS* nxt) __attribute__((always_inline)) {
-    read_frags<T>(f1, cur, lo, 1);
-    mfma_step<T>(acc, f0);
-    sched_step<NM, ND, 0>();
-    read_frags<T>(f0, cur, lo, 2);
-    mfma_step<T>(acc, f1);
-    sched_step<NM, ND, 0>();
-    read_frags<T>(f1, cur, lo, 3);
-    mfma_step<T>(acc, f0);
-    sched_step<NM, ND, 0>();
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    lds_barrier();
-    issue(s + 2, cur);
-    read_frags<T>(f0, nxt, lo, 0);
-    mfma_step<T>(acc, f1);
-    sched_step<NM, ND, NV>();
+  // One panel from stage `cur`, with panel s+1 in `nxt`; `prev` held panel s-1.
+  //  * NS == 2: past the barrier in the last k step, `cur` (just consumed) is refilled with
+  //    panel s+2.
+  //  * NS >= 3: `prev` is refilled with panel s+NS-1 at the start of the panel, its loads
+  //    spread over the first k step's MFMAs.  Every wave finished reading `prev` before the
+  //    previous panel's barrier (which waits for the wave's own LDS reads), so no further
+  //    synchronisation is needed, and this panel's barrier only has to see panel s+1 land.
+  auto panel = [&](int s, char GK_LDS* cur, char GK_LDS* nxt, char GK_LDS* prev)
+                   __attribute__((always_inline)) {
+#pragma unroll
+    for (int kk = 0; kk + 1 < KS; ++kk) {
+      if constexpr (NS >= 3) {
+        if (kk == 0) issue(s + NS - 1, prev);
+      }
+      read_frags<T>(f[(kk + 1) & 1], cur, lo, kk + 1);
+      mfma_step<T>(acc, f[kk & 1]);
+      if constexpr (NS >= 3) {
+        if (kk == 0)
+          sched_step<NM, ND, NV>();
+        else
+          sched_step<NM, ND, 0>();
+      } else {
+        sched_step<NM, ND, 0>();
+      }
+    }
+    wait_vmcnt<(NS - 2) * NV>();   // panel s+1 has landed (this wave's part)
+    lds_barrier();                 // ... every wave's part
+    if constexpr (NS == 2) issue(s + NS, cur);
+    read_frags<T>(f[0], nxt, lo, 0);
+    mfma_step<T>(acc, f[1]);
+    sched_step<NM, ND, NS == 2 ? NV : 0>();
   };
 
-  // Panels run in pairs (stage 0, then stage 1) with no branch inside a pair.  An odd panel
-  // count is padded with one all-zero panel, which adds exactly +0 to every accumulator.
   if (nk > 0) {
-    issue(0, S0);
-    issue(1, S1);
-    if constexpr (NV == 16)
-      asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
-    else if constexpr (NV == 12)
-      asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
-    else if constexpr (NV == 8)
-      asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-    else if constexpr (NV == 6)
-      asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
-    else
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // NS == 2 starts with both stages loaded; NS >= 3 with all but the last (the first
+    // panel refills it).
+    constexpr int kPre = NS == 2 ? 2 : NS - 1;
+#pragma unroll
+    for (int j = 0; j < kPre; ++j) issue(j, S[j]);
+    wait_vmcnt<(kPre - 1) * NV>();
     lds_barrier();
-    read_frags<T>(f0, S0, lo, 0);
+    read_frags<T>(f[0], S[0], lo, 0);
   }
-  for (int s = 0; s < nk; s += 2) {
-    panel(s, S0, S1);
-    panel(s + 1, S1, S0);
+  for (int s = 0; s < nk; s += NS) {
+#pragma unroll
+    for (int j = 0; j < NS; ++j) panel(s + j, S[j], S[(j + 1) % NS], S[(j + NS - 1) % NS]);
   }
   // The last refills (of panels past the end) must land before the workgroup's LDS is freed.
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  wait_vmcnt<0>();
   store_tile<T>(p, acc, m0, n0, wm, wn, lane);
 }
 

@@ -54,19 +54,22 @@ enum {
 };
 
 /* Tile configurations (BM x BN x BK; 256 threads = 4 wavefronts of 64 lanes in a 2 x 2
- * arrangement, each accumulating a (BM/2) x (BN/2) block with 32x32x16 fp16 MFMAs). */
+ * arrangement, each accumulating a (BM/2) x (BN/2) block with 32x32x16 fp16 MFMAs).  BK is
+ * the k depth of one LDS-staged panel of the aligned path (2 LDS stages at BK = 64, 4 at
+ * BK = 32); the generic path stages 64-deep panels for every tile. */
 enum {
     GEMM_F16F32_TILE_AUTO = 0,
     GEMM_F16F32_TILE_256x256x64 = 1,
     GEMM_F16F32_TILE_128x128x64 = 2,
     GEMM_F16F32_TILE_128x64x64 = 3,
-    GEMM_F16F32_TILE_256x128x64 = 4
+    GEMM_F16F32_TILE_256x128x64 = 4,
+    GEMM_F16F32_TILE_256x256x32 = 5
 };
 
 /* Kernel families. */
 enum {
-    GEMM_F16F32_PATH_ALIGNED = 0, /* 16-byte aligned A/B, lda/ldb % 8 == 0, N % 8 == 0,
-                                     K % BK == 0: 128-bit direct global->LDS loads */
+    GEMM_F16F32_PATH_ALIGNED = 0, /* 16-byte aligned A/B, lda % 8 == 0, ldb % 8 == 0,
+                                     K % BK == 0: 128-bit buffer->LDS loads */
     GEMM_F16F32_PATH_GENERIC = 1  /* anything else: bounds-checked buffer loads, K-tail
                                      zero fill, any leading dimension and alignment */
 };
@@ -83,7 +86,7 @@ typedef struct gemm_f16f32_opts {
 typedef struct gemm_f16f32_plan_info {
     int32_t path;          /* GEMM_F16F32_PATH_* */
     int32_t tile;          /* GEMM_F16F32_TILE_* actually used */
-    int32_t bm, bn, bk;    /* tile sizes */
+    int32_t bm, bn, bk;    /* tile sizes (bk: panel depth of the kernel chosen) */
     int32_t group_m;       /* GROUP_SIZE_M actually used */
     int32_t xcd_remap;     /* 1 if the XCD permutation is applied */
     int32_t num_pid_m;     /* cdiv(M, bm) */

@@ -76,7 +76,7 @@ def test_empty_problems_are_noops():
 
 def test_option_errors():
     base = (64, 64, 64, PA, PB, PC, 64, 64, 64)
-    for bad in ({"tile": 9}, {"group_m": -1}, {"xcd_remap": 3}, {"force_generic": 2}):
+    for bad in ({"tile": 6}, {"group_m": -1}, {"xcd_remap": 3}, {"force_generic": 2}):
         assert g.gemm_f16f32_plan(*base, opts=bad)[0] == g.ERR_OPTS
         assert g.gemm_f16f32_ex(*base, None, bad) == g.ERR_OPTS
 
@@ -115,7 +115,9 @@ def test_aligned_path_conditions():
     assert plan(256, 256, 256)["path"] == g.PATH_ALIGNED
     assert plan(256, 256, 256, force_generic=1)["path"] == g.PATH_GENERIC
     assert plan(256, 256, 200)["path"] == g.PATH_GENERIC          # K % 64
-    assert plan(256, 250, 256, ldb=256, ldc=256)["path"] == g.PATH_GENERIC  # N % 8
+    assert plan(256, 250, 256, ldb=256, ldc=256)["path"] == g.PATH_ALIGNED  # N tail: masked
+    assert plan(256, 256, 96, tile=g.TILE_256x256x32)["path"] == g.PATH_ALIGNED
+    assert plan(256, 256, 96, tile=g.TILE_256x256x64)["path"] == g.PATH_GENERIC
     assert plan(256, 256, 256, lda=260)["path"] == g.PATH_GENERIC  # lda % 8
     assert plan(256, 256, 256, a=PA + 2)["path"] == g.PATH_GENERIC  # alignment
     assert plan(300, 256, 256)["path"] == g.PATH_ALIGNED           # M tail is clamped
