@@ -245,7 +245,7 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": args.workload, "M": r["M"], "N": r["N"], "K": r["K"],
-            "accumulate": "f32", "path": ["aligned", "generic"][plan["path"]],
+            "accumulate": "f32", "path": ["dma", "generic"][plan["path"]],
             "tile": f"{plan['bm']}x{plan['bn']}x{plan['bk']}", "group_m": plan["group_m"],
             "xcd_remap": plan["xcd_remap"], "workgroups": plan["num_programs"],
         },

@@ -23,7 +23,7 @@ ERR_DIM, ERR_NULL, ERR_LD, ERR_OVERLAP, ERR_OPTS, ERR_TOO_LARGE, ERR_HIP = range
  TILE_256x256x32) = range(6)
 TILES = {TILE_256x256x64: (256, 256), TILE_128x128x64: (128, 128), TILE_128x64x64: (128, 64),
          TILE_256x128x64: (256, 128), TILE_256x256x32: (256, 256)}
-PATH_ALIGNED, PATH_GENERIC = 0, 1
+PATH_DMA, PATH_GENERIC = 0, 1
 REMAP_DEFAULT, REMAP_ON, REMAP_OFF = 0, 1, 2
 
 

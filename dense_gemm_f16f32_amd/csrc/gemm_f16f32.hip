@@ -11,8 +11,8 @@ namespace {
 
 constexpr int kVersion = 100;  // 0.1.0
 
-// bk: panel depth of the aligned kernel (the generic kernel always uses 64-deep panels);
-// stages: LDS stages of the aligned kernel.
+// bk: panel depth of the DMA kernel (the generic kernel always uses 64-deep panels);
+// stages: LDS stages of the DMA kernel.
 struct TileDesc {
   int id, bm, bn, bk, stages, default_group;
 };
@@ -84,14 +84,13 @@ int plan(int64_t M, int64_t N, int64_t K, const uint16_t* A, const uint16_t* B,
   // 32-bit in-kernel offsets: one panel's rows of A (bm x lda) and of B (64 x ldb).
   if ((int64_t)t->bm * lda >= kMax || (int64_t)gk::kBK * ldb >= kMax) return GEMM_F16F32_ERR_TOO_LARGE;
 
-  const bool aligned = !o.force_generic && ((uintptr_t)A % 16 == 0) && ((uintptr_t)B % 16 == 0) &&
-                       lda % 8 == 0 && ldb % 8 == 0 && K % t->bk == 0;
+  const bool dma = !o.force_generic;
   gemm_f16f32_plan_info r;
-  r.path = aligned ? GEMM_F16F32_PATH_ALIGNED : GEMM_F16F32_PATH_GENERIC;
+  r.path = dma ? GEMM_F16F32_PATH_DMA : GEMM_F16F32_PATH_GENERIC;
   r.tile = t->id;
   r.bm = t->bm;
   r.bn = t->bn;
-  r.bk = aligned ? t->bk : gk::kBK;
+  r.bk = dma ? t->bk : gk::kBK;
   r.group_m = o.group_m ? o.group_m : t->default_group;
   r.xcd_remap = (o.xcd_remap == 2) ? 0 : 1;
   r.num_pid_m = emptyC ? 0 : (int32_t)cdiv(M, t->bm);
@@ -107,8 +106,8 @@ template <int BM, int BN, int BK, int NS>
 hipError_t launch(const gemm_f16f32_plan_info& r, const gk::Args& a, bool odd,
                   hipStream_t stream) {
   const dim3 grid(r.num_programs), block(gk::kThreads);
-  if (r.path == GEMM_F16F32_PATH_ALIGNED)
-    hipLaunchKernelGGL((gk::gemm_aligned<BM, BN, BK, NS>), grid, block, 0, stream, a);
+  if (r.path == GEMM_F16F32_PATH_DMA)
+    hipLaunchKernelGGL((gk::gemm_dma<BM, BN, BK, NS>), grid, block, 0, stream, a);
   else if (odd)
     hipLaunchKernelGGL((gk::gemm_generic<BM, BN, true>), grid, block, 0, stream, a);
   else

@@ -293,20 +293,29 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 
 // ---------------------------------------------------------------------------------------
-// Aligned path: A and B 16-byte aligned, lda % 8 == 0, ldb % 8 == 0, K % BK == 0.  Each
-// thread issues A_LD + B_LD 16-byte buffer->LDS loads per panel; the buffer resources end at
-// the matrices' last elements, so nothing past them is ever read.
+// DMA path (any shape, any 2-byte alignment, any leading dimension).
+//
+// Panels are BK deep.  When BK does not divide K, panel 0 is a "head" that holds the first
+// K mod BK values of k at its end and zeros in front: the run is then the same, bit for bit,
+// as a run on operands zero-padded in front of k to a multiple of BK, and every later panel
+// is a full one.  Full panels are loaded with 16-byte buffer->LDS DMA (A: rows of 16-byte
+// chunks, B: 16-byte chunks of rows); the buffer resources end at the matrices' last
+// elements, so rows past M read as zeros and nothing past the matrices is read.  Columns
+// past N read whatever lies there and only feed results that are never stored.  The head is
+// loaded through registers, A element by element (so nothing before A's first element is
+// ever addressed), and written to LDS in the same layout.
 //
 // Pipeline (per wave), NS LDS stages, panel s in stage s mod NS: the operands of k step kk+1
 // are read from LDS while the MFMAs of step kk run.  The one barrier per panel sits in the
 // last k step, after that step's operands are in registers; past it the first operands of
-// panel s+1 are read.  Stage refills: see `panel` below.  The stages are separate LDS objects and the loop
-// is unrolled by NS, so the compiler can see that a refill never aliases the stage being read
-// and does not wait for it.  Panels past the end get empty buffer resources: they load zeros,
-// touch no memory and add exactly +0, which keeps the loop free of branches.
+// panel s+1 are read.  Stage refills: see `panel` below.  The stages are separate LDS objects
+// and the loop is unrolled by NS, so the compiler can see that a refill never aliases the
+// stage being read and does not wait for it.  Panels past the end get empty buffer
+// resources: they load zeros, touch no memory and add exactly +0, which keeps the loop free
+// of branches.
 // ---------------------------------------------------------------------------------------
 template <int BM, int BN, int BK, int NS>
-__global__ void __launch_bounds__(kThreads) gemm_aligned(Args p) {
+__global__ void __launch_bounds__(kThreads) gemm_dma(Args p) {
   using T = Tile<BM, BN, BK>;
   constexpr int KS = BK / 16;              // k steps per panel
   constexpr int NM = T::TM * T::TN;        // MFMAs per k step
@@ -329,9 +338,9 @@ __global__ void __launch_bounds__(kThreads) gemm_aligned(Args p) {
                pid, pid_m, pid_n);
   const int m0 = pid_m * BM, n0 = pid_n * BN;
 
-  // Per-thread byte offsets of its load slots, relative to the panel's corner.  Rows past M
-  // fall outside the buffer resource and read as zeros; columns past N read whatever lies
-  // there and only feed results that are never stored.
+  // This thread's load slots: slot q = (i*4 + w)*64 + lane of a stage holds logical chunk
+  // (row, chunk) of A (or B) as given by the swizzles.  Byte offsets relative to the panel's
+  // corner.
   uint32_t offA[T::A_LD], offB[T::B_LD];
 #pragma unroll
   for (int i = 0; i < T::A_LD; ++i) {
@@ -349,15 +358,51 @@ __global__ void __launch_bounds__(kThreads) gemm_aligned(Args p) {
   // Extents (elements from each matrix's first element to one past its last).
   const int64_t extA = (int64_t)(p.M - 1) * p.lda + p.K;
   const int64_t extB = (int64_t)(p.K - 1) * p.ldb + p.N;
-  const int nk = p.K / BK;
+  const int rk = p.K % BK;                       // depth of the head panel (0: none)
+  const int np = p.K / BK + (rk ? 1 : 0);        // panels
+  const int kofs = rk ? rk - BK : 0;             // panel s covers k in [kofs + s BK, + BK)
 
-  // Panel s of A starts at A[m0][BK s], of B at B[BK s][n0]; each gets a buffer resource
-  // (scalar registers) that ends at its matrix's last element.  A panel index s >= nk gets an
-  // empty resource: its loads touch no memory and deposit zeros.
+  // The last panel's copies of A's last element A[M-1][K-1] and B's last element
+  // B[K-1][N-1].  A 16-byte load that starts 2 bytes into a dword is range-checked dword by
+  // dword from its own start, so when a matrix ends on a 4-byte boundary the dword holding its
+  // last element reaches 2 bytes past the end and reads as zero.  The thread whose load slot
+  // holds that element (local k = BK-1 of the last panel, for tiles that contain row M-1 or
+  // column N-1) rewrites it from an exact 2-byte load once the panel has landed.
+  int patch_a = -1, patch_b = -1;    // LDS byte offsets within a stage, or -1
+  uint16_t last_a = 0, last_b = 0;
+  {
+    const int t = threadIdx.x;
+    const int rl = p.M - 1 - m0;
+    if (p.K > 0 && rl < BM) {
+      const int q = rl * T::CA + ((T::CA - 1) ^ swz_a<T::CA>(rl));
+      if ((q & (kThreads - 1)) == t) {
+        patch_a = q * 16 + 7 * 2;
+        last_a = __builtin_amdgcn_raw_buffer_load_b16(
+            make_rsrc(p.A, 2 * extA), 2u * (uint32_t)((int64_t)(p.M - 1) * p.lda + p.K - 1), 0, 0);
+      }
+    }
+    const int cl = p.N - 1 - n0;
+    if (p.K > 0 && cl < BN) {
+      const int q = (BK - 1) * T::CB + ((cl >> 3) ^ swz_b<T::CB>(BK - 1));
+      if ((q & (kThreads - 1)) == t) {
+        patch_b = T::A_BYTES + q * 16 + (cl & 7) * 2;
+        last_b = __builtin_amdgcn_raw_buffer_load_b16(
+            make_rsrc(p.B, 2 * extB), 2u * (uint32_t)((int64_t)(p.K - 1) * p.ldb + p.N - 1), 0, 0);
+      }
+    }
+  }
+  auto patch = [&](char GK_LDS* base) __attribute__((always_inline)) {
+    if (patch_a >= 0) *(uint16_t GK_LDS*)(base + patch_a) = last_a;
+    if (patch_b >= 0) *(uint16_t GK_LDS*)(base + patch_b) = last_b;
+  };
+
+  // Full panel s (k0 = kofs + s BK >= 0): DMA into `base`.  Panels past the end get an empty
+  // resource: their loads touch no memory and deposit zeros.
   auto issue = [&](int s, char GK_LDS* base) __attribute__((always_inline)) {
-    const bool live = s < nk;
-    const int64_t a0 = (int64_t)m0 * p.lda + (int64_t)s * BK;
-    const int64_t b0 = (int64_t)s * BK * p.ldb + n0;
+    const bool live = s < np;
+    const int64_t k0 = (int64_t)kofs + (int64_t)s * BK;
+    const int64_t a0 = (int64_t)m0 * p.lda + k0;
+    const int64_t b0 = k0 * p.ldb + n0;
     const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.A + (live ? a0 : 0), live ? 2 * (extA - a0) : 0);
     const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.B + (live ? b0 : 0), live ? 2 * (extB - b0) : 0);
 #pragma unroll
@@ -366,6 +411,44 @@ __global__ void __launch_bounds__(kThreads) gemm_aligned(Args p) {
 #pragma unroll
     for (int i = 0; i < T::B_LD; ++i)
       buffer_load_lds16(rb, (void GK_LDS*)(base + T::A_BYTES + (i * 4 + w) * 1024), offB[i]);
+  };
+
+  // Head panel (k0 = kofs < 0): the same slots, through registers; k < 0 is zero.
+  auto head = [&](char GK_LDS* base) __attribute__((always_inline)) {
+    const int64_t a0 = (int64_t)m0 * p.lda;
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.A + a0, 2 * (extA - a0));
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.B + n0, 2 * (extB - n0));
+    u32x4 va[T::A_LD], vb[T::B_LD];
+#pragma unroll
+    for (int i = 0; i < T::A_LD; ++i) {
+      const int q = (i * 4 + w) * 64 + lane;
+      const int r = q / T::CA, c = (q % T::CA) ^ swz_a<T::CA>(r);
+      uint16_t h[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int k = kofs + c * 8 + e;
+        h[e] = k >= 0 ? __builtin_amdgcn_raw_buffer_load_b16(
+                            ra, 2u * ((uint32_t)r * (uint32_t)p.lda + (uint32_t)k), 0, 0)
+                      : (uint16_t)0;
+      }
+#pragma unroll
+      for (int d = 0; d < 4; ++d) va[i][d] = (uint32_t)h[2 * d] | ((uint32_t)h[2 * d + 1] << 16);
+    }
+#pragma unroll
+    for (int i = 0; i < T::B_LD; ++i) {
+      const int q = (i * 4 + w) * 64 + lane;
+      const int k = q / T::CB, c = (q % T::CB) ^ swz_b<T::CB>(k);
+      const int kr = kofs + k;
+      vb[i] = kr >= 0 ? __builtin_amdgcn_raw_buffer_load_b128(
+                            rb, 2u * ((uint32_t)kr * (uint32_t)p.ldb + (uint32_t)(c * 8)), 0, 0)
+                      : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int i = 0; i < T::A_LD; ++i)
+      *(u32x4 GK_LDS*)(base + ((i * 4 + w) * 64 + lane) * 16) = va[i];
+#pragma unroll
+    for (int i = 0; i < T::B_LD; ++i)
+      *(u32x4 GK_LDS*)(base + T::A_BYTES + ((i * 4 + w) * 64 + lane) * 16) = vb[i];
   };
 
   float16v acc[T::TM][T::TN];
@@ -406,6 +489,7 @@ __global__ void __launch_bounds__(kThreads) gemm_aligned(Args p) {
       }
     }
     wait_vmcnt<(NS - 2) * NV>();   // panel s+1 has landed (this wave's part)
+    if (s + 2 == np) patch(nxt);   // panel s+1 is the last one
     lds_barrier();                 // ... every wave's part
     if constexpr (NS == 2) issue(s + NS, cur);
     read_frags<T>(f[0], nxt, lo, 0);
@@ -413,17 +497,22 @@ __global__ void __launch_bounds__(kThreads) gemm_aligned(Args p) {
     sched_step<NM, ND, NS == 2 ? NV : 0>();
   };
 
-  if (nk > 0) {
-    // NS == 2 starts with both stages loaded; NS >= 3 with all but the last (the first
+  if (np > 0) {
+    // NS == 2 starts with both stages filled; NS >= 3 with all but the last (the first
     // panel refills it).
     constexpr int kPre = NS == 2 ? 2 : NS - 1;
+    if (rk)
+      head(S[0]);
+    else
+      issue(0, S[0]);
 #pragma unroll
-    for (int j = 0; j < kPre; ++j) issue(j, S[j]);
+    for (int j = 1; j < kPre; ++j) issue(j, S[j]);
     wait_vmcnt<(kPre - 1) * NV>();
+    if (np == 1) patch(S[0]);
     lds_barrier();
     read_frags<T>(f[0], S[0], lo, 0);
   }
-  for (int s = 0; s < nk; s += NS) {
+  for (int s = 0; s < np; s += NS) {
 #pragma unroll
     for (int j = 0; j < NS; ++j) panel(s + j, S[j], S[(j + 1) % NS], S[(j + NS - 1) % NS]);
   }

@@ -66,12 +66,13 @@ enum {
     GEMM_F16F32_TILE_256x256x32 = 5
 };
 
-/* Kernel families. */
+/* Kernel families.  Both accept any shape, leading dimension and 2-byte alignment. */
 enum {
-    GEMM_F16F32_PATH_ALIGNED = 0, /* 16-byte aligned A/B, lda % 8 == 0, ldb % 8 == 0,
-                                     K % BK == 0: 128-bit buffer->LDS loads */
-    GEMM_F16F32_PATH_GENERIC = 1  /* anything else: bounds-checked buffer loads, K-tail
-                                     zero fill, any leading dimension and alignment */
+    GEMM_F16F32_PATH_DMA = 0,     /* default: 16-byte buffer->LDS loads of full BK-deep
+                                     panels; when BK does not divide K the first panel holds
+                                     the K mod BK leading k values, zero-padded in front */
+    GEMM_F16F32_PATH_GENERIC = 1  /* only when forced: panels staged through registers,
+                                     zero fill past K in the last panel */
 };
 
 /* Options for gemm_f16f32_ex.  Zero-initialised options mean "library default" throughout. */
@@ -79,7 +80,7 @@ typedef struct gemm_f16f32_opts {
     int32_t tile;          /* GEMM_F16F32_TILE_*; 0 = chosen from the shape */
     int32_t group_m;       /* GROUP_SIZE_M >= 1; 0 = library default for the tile */
     int32_t xcd_remap;     /* 0 = default (on), 1 = on, 2 = off (hardware id = program id) */
-    int32_t force_generic; /* 1 = use the generic path even when the aligned one applies */
+    int32_t force_generic; /* 1 = use the generic (register-staged) path */
 } gemm_f16f32_opts;
 
 /* What a call with these arguments would launch (filled by gemm_f16f32_plan). */

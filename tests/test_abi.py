@@ -98,27 +98,30 @@ def plan(M, N, K, lda=None, ldb=None, ldc=None, a=PA, b=PB, c=PC, **opts):
 
 def test_plans_for_the_five_workloads():
     p = plan(512, 512, 512)
-    assert (p["path"], p["bm"], p["bn"], p["num_programs"]) == (g.PATH_ALIGNED, 128, 64, 32)
+    assert (p["path"], p["bm"], p["bn"], p["num_programs"]) == (g.PATH_DMA, 128, 64, 32)
     p = plan(1024, 768, 128, tile=g.TILE_128x64x64, group_m=2)
     assert (p["num_pid_m"], p["num_pid_n"], p["num_programs"], p["group_m"]) == (8, 12, 96, 2)
     p = plan(4096, 4096, 4096)
-    assert (p["path"], p["bm"], p["bn"], p["num_programs"]) == (g.PATH_ALIGNED, 256, 256, 256)
+    assert (p["path"], p["bm"], p["bn"], p["num_programs"]) == (g.PATH_DMA, 256, 256, 256)
     p = plan(8192, 8192, 8192)
-    assert (p["path"], p["bm"], p["bn"], p["num_programs"]) == (g.PATH_ALIGNED, 256, 256, 1024)
+    assert (p["path"], p["bm"], p["bn"], p["num_programs"]) == (g.PATH_DMA, 256, 256, 1024)
     assert p["xcd_remap"] == 1
     p = plan(4095, 4097, 4093, group_m=6)
     assert (p["path"], p["num_pid_m"], p["num_pid_n"], p["num_programs"]) == \
-        (g.PATH_GENERIC, 16, 17, 272)
+        (g.PATH_DMA, 16, 17, 272)
 
 
-def test_aligned_path_conditions():
-    assert plan(256, 256, 256)["path"] == g.PATH_ALIGNED
-    assert plan(256, 256, 256, force_generic=1)["path"] == g.PATH_GENERIC
-    assert plan(256, 256, 200)["path"] == g.PATH_GENERIC          # K % 64
-    assert plan(256, 250, 256, ldb=256, ldc=256)["path"] == g.PATH_ALIGNED  # N tail: masked
-    assert plan(256, 256, 96, tile=g.TILE_256x256x32)["path"] == g.PATH_ALIGNED
-    assert plan(256, 256, 96, tile=g.TILE_256x256x64)["path"] == g.PATH_GENERIC
-    assert plan(256, 256, 256, lda=260)["path"] == g.PATH_GENERIC  # lda % 8
-    assert plan(256, 256, 256, a=PA + 2)["path"] == g.PATH_GENERIC  # alignment
-    assert plan(300, 256, 256)["path"] == g.PATH_ALIGNED           # M tail is clamped
+def test_path_selection():
+    """The DMA path takes every shape, leading dimension and 2-byte alignment; the generic
+    path runs only when forced.  bk reports the panel depth of the kernel chosen."""
+    for kw in ({}, {"K": 200}, {"N": 250, "ldb": 256, "ldc": 256}, {"lda": 260},
+               {"a": PA + 2}, {"b": PB + 6, "ldb": 257}, {"M": 300}):
+        args = dict(M=256, N=256, K=256)
+        args.update(kw)
+        M, N, K = args.pop("M"), args.pop("N"), args.pop("K")
+        p = plan(M, N, K, **args)
+        assert p["path"] == g.PATH_DMA and p["bk"] == 64, kw
+    assert plan(256, 256, 96, tile=g.TILE_256x256x32)["bk"] == 32
+    p = plan(256, 256, 256, force_generic=1)
+    assert p["path"] == g.PATH_GENERIC and p["bk"] == 64
     assert plan(256, 256, 256, xcd_remap=2)["xcd_remap"] == 0

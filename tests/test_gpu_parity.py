@@ -121,8 +121,8 @@ def test_large_workload_sampled(name):
                                   opts=opts or None)
     assert rc == g.OK
     if name.startswith("gemm4095"):
-        # ragged: generic path, 16 x 17 tiles, and G = 6 leaves a last group of 4 rows
-        assert info["path"] == g.PATH_GENERIC and info["num_pid_m"] % 6 == 4
+        # ragged: 16 x 17 tiles, and G = 6 leaves a last group of 4 rows
+        assert info["num_pid_m"] % 6 == 4
     C = from_dev(run(to_dev(A), to_dev(B), M, N, K, **opts))
     assert not np.isnan(f64(C)).any()
     r, c = sample_positions(M, N, info["bm"], info["bn"], 6, seed)
@@ -131,22 +131,34 @@ def test_large_workload_sampled(name):
     assert checksum_ok(A, B, C), name
 
 
-def test_ragged_equals_zero_padded():
-    """The masked run equals the aligned run on zero-padded operands, bit for bit: zeros add
-    +0 to the same fp32 sums in the same order."""
+@pytest.mark.parametrize("tile", [g.TILE_256x256x64, g.TILE_256x256x32])
+def test_ragged_equals_front_padded(tile):
+    """The ragged run equals, bit for bit, a run on operands zero-padded to tile multiples:
+    in front of k (the DMA path puts the K mod BK leading k values at the end of its first
+    panel), after the last row of A and after the last column of B.  Zeros add +0 to the same
+    fp32 sums in the same order."""
     _, M, N, K, dist, seed = workload("gemm4095x4097x4093_n")
     A, B = operands(M, N, K, dist, seed)
-    Mp, Np, Kp = 4096, 4104, 4096
+    bk = 64 if tile == g.TILE_256x256x64 else 32
+    pad = (-K) % bk
+    Mp, Np, Kp = 4096, 4104, K + pad
     Ap = np.zeros((Mp, Kp), np.uint16)
-    Ap[:M, :K] = A
+    Ap[:M, pad:] = A
     Bp = np.zeros((Kp, Np), np.uint16)
-    Bp[:K, :N] = B
-    opts = dict(tile=g.TILE_256x256x64, group_m=6)
+    Bp[pad:, :N] = B
+    opts = dict(tile=tile, group_m=6)
     C = from_dev(run(to_dev(A), to_dev(B), M, N, K, **opts))
-    rc, info = g.gemm_f16f32_plan(Mp, Np, Kp, 1 << 40, 2 << 40, 3 << 40, Kp, Np, Np, opts=opts)
-    assert info["path"] == g.PATH_ALIGNED
     Cp = from_dev(run(to_dev(Ap), to_dev(Bp), Mp, Np, Kp, **opts))
     assert np.array_equal(C, Cp[:M, :N])
+
+
+def test_ragged_generic_path_within_tolerance():
+    """The register-staged generic path on the ragged shape (its own k order)."""
+    _, M, N, K, dist, seed = workload("gemm4095x4097x4093_n")
+    A, B = operands(M, N, K, dist, seed)
+    C = from_dev(run(to_dev(A), to_dev(B), M, N, K, force_generic=1, group_m=6))
+    r, c = sample_positions(M, N, 256, 256, 4, 11)
+    assert_within_tolerance(C[r, c], oracle.gemm_sampled(A, B, r, c), "generic ragged")
 
 
 # ---------------------------------------------------------------------------------------
@@ -158,20 +170,23 @@ def ops2048():
     return A, B, to_dev(A), to_dev(B)
 
 
-def test_generic_path_bitwise_equals_aligned(ops2048):
+def test_paths_and_alignment_change_no_bit(ops2048):
+    """With 64-deep panels and K a multiple of 64 the DMA and generic paths add the same
+    products in the same order, so they agree bit for bit -- also on operands that start 2 or
+    6 bytes past an aligned address (rows only 2-byte aligned)."""
     A, B, Ad, Bd = ops2048
     ref = from_dev(run(Ad, Bd, 2048, 2048, 2048, tile=g.TILE_256x256x64))
     gen = from_dev(run(Ad, Bd, 2048, 2048, 2048, tile=g.TILE_256x256x64, force_generic=1))
     assert np.array_equal(ref, gen)
-    # operands starting 2 bytes past an aligned address (odd-offset rows in the generic path)
     Ab = torch.zeros(2048 * 2048 + 8, dtype=torch.int16, device="cuda")
     Bb = torch.zeros(2048 * 2048 + 8, dtype=torch.int16, device="cuda")
     Ab[1:1 + 2048 * 2048] = Ad.reshape(-1)
     Bb[3:3 + 2048 * 2048] = Bd.reshape(-1)
     Au = Ab[1:1 + 2048 * 2048].view(2048, 2048)
     Bu = Bb[3:3 + 2048 * 2048].view(2048, 2048)
-    odd = from_dev(run(Au, Bu, 2048, 2048, 2048, tile=g.TILE_256x256x64))
-    assert np.array_equal(ref, odd)
+    for fg in (0, 1):
+        odd = from_dev(run(Au, Bu, 2048, 2048, 2048, tile=g.TILE_256x256x64, force_generic=fg))
+        assert np.array_equal(ref, odd), fg
 
 
 def test_group_and_remap_change_no_bit(ops2048):
