@@ -20,11 +20,13 @@ LIB_PATH = os.path.join(PKG, "libgemm_f16f32.so")
 OK = 0
 ERR_DIM, ERR_NULL, ERR_LD, ERR_OVERLAP, ERR_OPTS, ERR_TOO_LARGE, ERR_HIP = range(-1, -8, -1)
 (TILE_AUTO, TILE_256x256x64, TILE_128x128x64, TILE_128x64x64, TILE_256x128x64,
- TILE_256x256x32) = range(6)
+ TILE_256x256x32, TILE_64x64x32, TILE_128x64x32) = range(8)
 TILES = {TILE_256x256x64: (256, 256), TILE_128x128x64: (128, 128), TILE_128x64x64: (128, 64),
-         TILE_256x128x64: (256, 128), TILE_256x256x32: (256, 256)}
+         TILE_256x128x64: (256, 128), TILE_256x256x32: (256, 256), TILE_64x64x32: (64, 64),
+         TILE_128x64x32: (128, 64)}
 PATH_DMA, PATH_GENERIC = 0, 1
 REMAP_DEFAULT, REMAP_ON, REMAP_OFF = 0, 1, 2
+SPLIT_DEFAULT, SPLIT_ON, SPLIT_OFF = 0, 1, 2
 
 
 class GemmError(RuntimeError):
@@ -35,13 +37,14 @@ class GemmError(RuntimeError):
 
 class Opts(ctypes.Structure):
     _fields_ = [("tile", ctypes.c_int32), ("group_m", ctypes.c_int32),
-                ("xcd_remap", ctypes.c_int32), ("force_generic", ctypes.c_int32)]
+                ("xcd_remap", ctypes.c_int32), ("force_generic", ctypes.c_int32),
+                ("split_edges", ctypes.c_int32)]
 
 
 class PlanInfo(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in ("path", "tile", "bm", "bn", "bk", "group_m",
                                               "xcd_remap", "num_pid_m", "num_pid_n",
-                                              "num_programs")]
+                                              "num_programs", "launches", "main_m", "main_n")]
 
     def as_dict(self) -> dict:
         return {n: getattr(self, n) for n, _ in self._fields_}
@@ -138,7 +141,7 @@ def matmul(a, b, out=None, *, M=None, N=None, K=None, stream=None, **opts):
 
     a, b, out: 2-D CUDA tensors of 16-bit elements (float16, or int16 holding fp16 bits),
     row-major with unit inner stride and any leading dimension.  opts: tile, group_m,
-    xcd_remap, force_generic (see include/gemm_f16f32.h).  Raises GemmError on a non-zero
+    xcd_remap, force_generic, split_edges (see include/gemm_f16f32.h).  Raises GemmError on a non-zero
     return code.  Launches on torch's current stream unless `stream` is given.
     """
     import torch

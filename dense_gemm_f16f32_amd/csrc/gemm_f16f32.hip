@@ -23,6 +23,8 @@ constexpr TileDesc kTiles[] = {
     {GEMM_F16F32_TILE_128x64x64, 128, 64, 64, 2, 4},
     {GEMM_F16F32_TILE_256x128x64, 256, 128, 64, 2, 8},
     {GEMM_F16F32_TILE_256x256x32, 256, 256, 32, 4, 8},
+    {GEMM_F16F32_TILE_64x64x32, 64, 64, 32, 5, 4},
+    {GEMM_F16F32_TILE_128x64x32, 128, 64, 32, 5, 4},
 };
 
 const TileDesc* find_tile(int id) {
@@ -34,11 +36,14 @@ const TileDesc* find_tile(int id) {
 int64_t cdiv(int64_t x, int64_t y) { return (x + y - 1) / y; }
 
 // Tile chosen from the shape: the largest tile whose grid still covers the 256 CUs about
-// once; smaller problems fall back to smaller tiles so that more CUs take part.
+// once; smaller problems fall back to smaller tiles so that more CUs take part.  Thin shapes
+// (a side of at most 64) are latency bound over their whole K and take the 64 x 64 tile
+// with 32-deep panels and 5 LDS stages, which keeps 4 panels in flight.
 int auto_tile(int64_t M, int64_t N) {
   if (cdiv(M, 256) * cdiv(N, 256) >= 240) return GEMM_F16F32_TILE_256x256x64;
   if (cdiv(M, 256) * cdiv(N, 128) >= 240) return GEMM_F16F32_TILE_256x128x64;
   if (cdiv(M, 128) * cdiv(N, 128) >= 120) return GEMM_F16F32_TILE_128x128x64;
+  if (M <= 64 || N <= 64) return GEMM_F16F32_TILE_64x64x32;
   return GEMM_F16F32_TILE_128x64x64;
 }
 
@@ -55,10 +60,54 @@ bool overlaps(const void* a, uint64_t na, const void* b, uint64_t nb) {
   return x < y + nb && y < x + na;
 }
 
-int plan(int64_t M, int64_t N, int64_t K, const uint16_t* A, const uint16_t* B,
-         const uint16_t* C, int64_t lda, int64_t ldb, int64_t ldc, const gemm_f16f32_opts* opts,
-         gemm_f16f32_plan_info* info) {
+// One launch over an M x N block of C (all of it, or one part of an edge split).
+struct Part {
+  int64_t m_off, n_off, M, N;
+  gemm_f16f32_plan_info r;
+};
+
+// Fills r for one launch of tile `tile` over M x N (no argument checks here).
+int plan_launch(int64_t M, int64_t N, int64_t lda, int64_t ldb, const TileDesc* t,
+                const gemm_f16f32_opts& o, gemm_f16f32_plan_info* r) {
   const int64_t kMax = (int64_t)1 << 31;
+  // 32-bit in-kernel offsets: one panel's rows of A (bm x lda) and of B (64 x ldb).
+  if ((int64_t)t->bm * lda >= kMax || (int64_t)gk::kBK * ldb >= kMax)
+    return GEMM_F16F32_ERR_TOO_LARGE;
+  const bool dma = !o.force_generic;
+  r->path = dma ? GEMM_F16F32_PATH_DMA : GEMM_F16F32_PATH_GENERIC;
+  r->tile = t->id;
+  r->bm = t->bm;
+  r->bn = t->bn;
+  r->bk = dma ? t->bk : gk::kBK;
+  r->group_m = o.group_m ? o.group_m : t->default_group;
+  r->xcd_remap = (o.xcd_remap == 2) ? 0 : 1;
+  const bool empty = (M == 0 || N == 0);
+  r->num_pid_m = empty ? 0 : (int32_t)cdiv(M, t->bm);
+  r->num_pid_n = empty ? 0 : (int32_t)cdiv(N, t->bn);
+  const int64_t P = (int64_t)r->num_pid_m * r->num_pid_n;
+  if (P >= kMax) return GEMM_F16F32_ERR_TOO_LARGE;
+  r->num_programs = (int32_t)P;
+  r->launches = empty ? 0 : 1;
+  r->main_m = (int32_t)M;
+  r->main_n = (int32_t)N;
+  return GEMM_F16F32_OK;
+}
+
+// Argument checks, tile choice and the edge split.  parts[0] is the main block; parts[1..]
+// are the thin strips (right, bottom, corner) when the split applies.  Returns the number of
+// parts through *nparts.
+//
+// Edge split: when the last tile column holds at most a quarter of a tile's columns (or the
+// last tile row a quarter of its rows) and the problem is large, those tiles would each do a
+// full tile's work for a sliver of C and often cost a whole extra wave of workgroups.  The
+// sliver is then computed by separate launches with tiles chosen for its own shape.  Every
+// element's k-sum is the same sequence of MFMA steps whatever the tile, so results do not
+// change.
+int plan_parts(int64_t M, int64_t N, int64_t K, const uint16_t* A, const uint16_t* B,
+               const uint16_t* C, int64_t lda, int64_t ldb, int64_t ldc,
+               const gemm_f16f32_opts* opts, Part* parts, int* nparts) {
+  const int64_t kMax = (int64_t)1 << 31;
+  *nparts = 0;
   if (M < 0 || N < 0 || K < 0 || M >= kMax || N >= kMax || K >= kMax) return GEMM_F16F32_ERR_DIM;
   if (lda < (K > 1 ? K : 1) || ldb < (N > 1 ? N : 1) || ldc < (N > 1 ? N : 1))
     return GEMM_F16F32_ERR_LD;
@@ -67,11 +116,11 @@ int plan(int64_t M, int64_t N, int64_t K, const uint16_t* A, const uint16_t* B,
   if (!emptyC && K > 0 && (A == nullptr || B == nullptr)) return GEMM_F16F32_ERR_NULL;
   if (((uintptr_t)A | (uintptr_t)B | (uintptr_t)C) & 1) return GEMM_F16F32_ERR_OPTS;
 
-  gemm_f16f32_opts o = {0, 0, 0, 0};
+  gemm_f16f32_opts o = {0, 0, 0, 0, 0};
   if (opts) o = *opts;
   if (o.tile != 0 && find_tile(o.tile) == nullptr) return GEMM_F16F32_ERR_OPTS;
   if (o.group_m < 0 || o.xcd_remap < 0 || o.xcd_remap > 2 || o.force_generic < 0 ||
-      o.force_generic > 1)
+      o.force_generic > 1 || o.split_edges < 0 || o.split_edges > 2)
     return GEMM_F16F32_ERR_OPTS;
 
   if (!emptyC) {
@@ -81,24 +130,34 @@ int plan(int64_t M, int64_t N, int64_t K, const uint16_t* A, const uint16_t* B,
   }
 
   const TileDesc* t = find_tile(o.tile ? o.tile : auto_tile(M, N));
-  // 32-bit in-kernel offsets: one panel's rows of A (bm x lda) and of B (64 x ldb).
-  if ((int64_t)t->bm * lda >= kMax || (int64_t)gk::kBK * ldb >= kMax) return GEMM_F16F32_ERR_TOO_LARGE;
-
-  const bool dma = !o.force_generic;
-  gemm_f16f32_plan_info r;
-  r.path = dma ? GEMM_F16F32_PATH_DMA : GEMM_F16F32_PATH_GENERIC;
-  r.tile = t->id;
-  r.bm = t->bm;
-  r.bn = t->bn;
-  r.bk = dma ? t->bk : gk::kBK;
-  r.group_m = o.group_m ? o.group_m : t->default_group;
-  r.xcd_remap = (o.xcd_remap == 2) ? 0 : 1;
-  r.num_pid_m = emptyC ? 0 : (int32_t)cdiv(M, t->bm);
-  r.num_pid_n = emptyC ? 0 : (int32_t)cdiv(N, t->bn);
-  const int64_t P = (int64_t)r.num_pid_m * r.num_pid_n;
-  if (P >= kMax) return GEMM_F16F32_ERR_TOO_LARGE;
-  r.num_programs = (int32_t)P;
-  if (info) *info = r;
+  int64_t Mm = M, Nm = N;
+  const bool split = o.split_edges == 1 || (o.split_edges == 0 && o.tile == 0);
+  if (split && !emptyC) {
+    const int64_t rm = M % t->bm, rn = N % t->bn;
+    const int64_t full_m = M / t->bm, full_n = N / t->bn;
+    if (full_m * full_n >= 128) {
+      if (rn > 0 && 4 * rn <= t->bn) Nm = N - rn;
+      if (rm > 0 && 4 * rm <= t->bm) Mm = M - rm;
+    }
+  }
+  Part* pp = parts;
+  pp->m_off = 0, pp->n_off = 0, pp->M = Mm, pp->N = Nm;
+  int rc = plan_launch(Mm, Nm, lda, ldb, t, o, &pp->r);
+  if (rc != GEMM_F16F32_OK) return rc;
+  ++pp;
+  const int64_t strips[3][4] = {{0, Nm, Mm, N - Nm}, {Mm, 0, M - Mm, Nm}, {Mm, Nm, M - Mm, N - Nm}};
+  gemm_f16f32_opts os = o;
+  os.tile = 0;
+  os.group_m = 0;
+  for (const auto& st : strips) {
+    if (st[2] == 0 || st[3] == 0) continue;
+    pp->m_off = st[0], pp->n_off = st[1], pp->M = st[2], pp->N = st[3];
+    rc = plan_launch(st[2], st[3], lda, ldb, find_tile(auto_tile(st[2], st[3])), os, &pp->r);
+    if (rc != GEMM_F16F32_OK) return rc;
+    ++pp;
+  }
+  *nparts = (int)(pp - parts);
+  parts[0].r.launches = emptyC ? 0 : *nparts;
   return GEMM_F16F32_OK;
 }
 
@@ -115,42 +174,26 @@ hipError_t launch(const gemm_f16f32_plan_info& r, const gk::Args& a, bool odd,
   return hipGetLastError();
 }
 
-}  // namespace
-
-extern "C" {
-
-int gemm_f16f32_plan(int64_t M, int64_t N, int64_t K, const uint16_t* A, const uint16_t* B,
-                     const uint16_t* C, int64_t lda, int64_t ldb, int64_t ldc,
-                     const gemm_f16f32_opts* opts, gemm_f16f32_plan_info* info) {
-  return plan(M, N, K, A, B, C, lda, ldb, ldc, opts, info);
-}
-
-int gemm_f16f32_ex(int64_t M, int64_t N, int64_t K, const uint16_t* A, const uint16_t* B,
-                   uint16_t* C, int64_t lda, int64_t ldb, int64_t ldc, void* stream,
-                   const gemm_f16f32_opts* opts) {
-  gemm_f16f32_plan_info r;
-  const int rc = plan(M, N, K, A, B, C, lda, ldb, ldc, opts, &r);
-  if (rc != GEMM_F16F32_OK) return rc;
+int launch_part(const Part& pt, int64_t K, const uint16_t* A, const uint16_t* B, uint16_t* C,
+                int64_t lda, int64_t ldb, int64_t ldc, hipStream_t s) {
+  const gemm_f16f32_plan_info& r = pt.r;
   if (r.num_programs == 0) return GEMM_F16F32_OK;
-
   gk::Args a;
-  a.A = A;
-  a.B = B;
-  a.C = C;
+  a.A = A + pt.m_off * lda;
+  a.B = B + pt.n_off;
+  a.C = C + pt.m_off * ldc + pt.n_off;
   a.lda = lda;
   a.ldb = ldb;
   a.ldc = ldc;
-  a.M = (int32_t)M;
-  a.N = (int32_t)N;
+  a.M = (int32_t)pt.M;
+  a.N = (int32_t)pt.N;
   a.K = (int32_t)K;
   a.num_pid_m = r.num_pid_m;
   a.num_pid_n = r.num_pid_n;
   a.group_m = r.group_m;
   a.xcd_remap = r.xcd_remap;
   a.num_programs = r.num_programs;
-  const bool odd = (((uintptr_t)A | (uintptr_t)B) & 3) != 0 || ((lda | ldb) & 1) != 0;
-  hipStream_t s = (hipStream_t)stream;
-
+  const bool odd = (((uintptr_t)a.A | (uintptr_t)a.B) & 3) != 0 || ((lda | ldb) & 1) != 0;
   hipError_t e = hipSuccess;
   switch (r.tile) {
     case GEMM_F16F32_TILE_256x256x64: e = launch<256, 256, 64, 2>(r, a, odd, s); break;
@@ -158,9 +201,37 @@ int gemm_f16f32_ex(int64_t M, int64_t N, int64_t K, const uint16_t* A, const uin
     case GEMM_F16F32_TILE_128x128x64: e = launch<128, 128, 64, 2>(r, a, odd, s); break;
     case GEMM_F16F32_TILE_128x64x64: e = launch<128, 64, 64, 2>(r, a, odd, s); break;
     case GEMM_F16F32_TILE_256x256x32: e = launch<256, 256, 32, 4>(r, a, odd, s); break;
+    case GEMM_F16F32_TILE_64x64x32: e = launch<64, 64, 32, 5>(r, a, odd, s); break;
+    case GEMM_F16F32_TILE_128x64x32: e = launch<128, 64, 32, 5>(r, a, odd, s); break;
     default: return GEMM_F16F32_ERR_OPTS;
   }
   return e == hipSuccess ? GEMM_F16F32_OK : GEMM_F16F32_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gemm_f16f32_plan(int64_t M, int64_t N, int64_t K, const uint16_t* A, const uint16_t* B,
+                     const uint16_t* C, int64_t lda, int64_t ldb, int64_t ldc,
+                     const gemm_f16f32_opts* opts, gemm_f16f32_plan_info* info) {
+  Part parts[4];
+  int n = 0;
+  const int rc = plan_parts(M, N, K, A, B, C, lda, ldb, ldc, opts, parts, &n);
+  if (rc == GEMM_F16F32_OK && info) *info = parts[0].r;
+  return rc;
+}
+
+int gemm_f16f32_ex(int64_t M, int64_t N, int64_t K, const uint16_t* A, const uint16_t* B,
+                   uint16_t* C, int64_t lda, int64_t ldb, int64_t ldc, void* stream,
+                   const gemm_f16f32_opts* opts) {
+  Part parts[4];
+  int n = 0;
+  int rc = plan_parts(M, N, K, A, B, C, lda, ldb, ldc, opts, parts, &n);
+  if (rc != GEMM_F16F32_OK) return rc;
+  for (int i = 0; i < n && rc == GEMM_F16F32_OK; ++i)
+    rc = launch_part(parts[i], K, A, B, C, lda, ldb, ldc, (hipStream_t)stream);
+  return rc;
 }
 
 int gemm_f16f32(int64_t M, int64_t N, int64_t K, const uint16_t* A, const uint16_t* B,

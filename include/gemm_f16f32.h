@@ -55,7 +55,7 @@ enum {
 
 /* Tile configurations (BM x BN x BK; 256 threads = 4 wavefronts of 64 lanes in a 2 x 2
  * arrangement, each accumulating a (BM/2) x (BN/2) block with 32x32x16 fp16 MFMAs).  BK is
- * the k depth of one LDS-staged panel of the aligned path (2 LDS stages at BK = 64, 4 at
+ * the k depth of one LDS-staged panel of the DMA path (2 LDS stages at BK = 64, 4 or 5 at
  * BK = 32); the generic path stages 64-deep panels for every tile. */
 enum {
     GEMM_F16F32_TILE_AUTO = 0,
@@ -63,7 +63,9 @@ enum {
     GEMM_F16F32_TILE_128x128x64 = 2,
     GEMM_F16F32_TILE_128x64x64 = 3,
     GEMM_F16F32_TILE_256x128x64 = 4,
-    GEMM_F16F32_TILE_256x256x32 = 5
+    GEMM_F16F32_TILE_256x256x32 = 5,
+    GEMM_F16F32_TILE_64x64x32 = 6,    /* 5 LDS stages */
+    GEMM_F16F32_TILE_128x64x32 = 7    /* 5 LDS stages */
 };
 
 /* Kernel families.  Both accept any shape, leading dimension and 2-byte alignment. */
@@ -81,9 +83,15 @@ typedef struct gemm_f16f32_opts {
     int32_t group_m;       /* GROUP_SIZE_M >= 1; 0 = library default for the tile */
     int32_t xcd_remap;     /* 0 = default (on), 1 = on, 2 = off (hardware id = program id) */
     int32_t force_generic; /* 1 = use the generic (register-staged) path */
+    int32_t split_edges;   /* 0 = default (on when the tile is chosen by the library), 1 = on,
+                              2 = off.  When the last tile column holds <= 1/4 of a tile's
+                              columns (or the last tile row <= 1/4 of its rows) and the rest
+                              spans >= 128 tiles, that sliver is computed by separate launches
+                              with tiles sized for it; results are unchanged. */
 } gemm_f16f32_opts;
 
-/* What a call with these arguments would launch (filled by gemm_f16f32_plan). */
+/* What a call with these arguments would launch (filled by gemm_f16f32_plan).  The fields
+ * describe the main launch, over C[0:main_m, 0:main_n]; edge strips, if any, follow it. */
 typedef struct gemm_f16f32_plan_info {
     int32_t path;          /* GEMM_F16F32_PATH_* */
     int32_t tile;          /* GEMM_F16F32_TILE_* actually used */
@@ -93,6 +101,9 @@ typedef struct gemm_f16f32_plan_info {
     int32_t num_pid_m;     /* cdiv(M, bm) */
     int32_t num_pid_n;     /* cdiv(N, bn) */
     int32_t num_programs;  /* num_pid_m * num_pid_n = workgroups launched (0 if none) */
+    int32_t launches;      /* kernel launches the call makes (1 + edge strips; 0 if empty) */
+    int32_t main_m;        /* rows of C covered by the launch described above */
+    int32_t main_n;        /* columns of C covered by the launch described above */
 } gemm_f16f32_plan_info;
 
 /*

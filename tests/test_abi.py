@@ -76,7 +76,8 @@ def test_empty_problems_are_noops():
 
 def test_option_errors():
     base = (64, 64, 64, PA, PB, PC, 64, 64, 64)
-    for bad in ({"tile": 6}, {"group_m": -1}, {"xcd_remap": 3}, {"force_generic": 2}):
+    for bad in ({"tile": 8}, {"group_m": -1}, {"xcd_remap": 3}, {"force_generic": 2},
+                {"split_edges": 3}):
         assert g.gemm_f16f32_plan(*base, opts=bad)[0] == g.ERR_OPTS
         assert g.gemm_f16f32_ex(*base, None, bad) == g.ERR_OPTS
 
@@ -107,8 +108,12 @@ def test_plans_for_the_five_workloads():
     assert (p["path"], p["bm"], p["bn"], p["num_programs"]) == (g.PATH_DMA, 256, 256, 1024)
     assert p["xcd_remap"] == 1
     p = plan(4095, 4097, 4093, group_m=6)
+    # the 1-column sliver is split off: the main launch covers 4095 x 4096 with 16 x 16 tiles
     assert (p["path"], p["num_pid_m"], p["num_pid_n"], p["num_programs"]) == \
-        (g.PATH_DMA, 16, 17, 272)
+        (g.PATH_DMA, 16, 16, 256)
+    assert (p["launches"], p["main_m"], p["main_n"]) == (2, 4095, 4096)
+    p = plan(4095, 4097, 4093, group_m=6, split_edges=g.SPLIT_OFF)
+    assert (p["num_pid_m"], p["num_pid_n"], p["num_programs"], p["launches"]) == (16, 17, 272, 1)
 
 
 def test_path_selection():
@@ -125,3 +130,20 @@ def test_path_selection():
     p = plan(256, 256, 256, force_generic=1)
     assert p["path"] == g.PATH_GENERIC and p["bk"] == 64
     assert plan(256, 256, 256, xcd_remap=2)["xcd_remap"] == 0
+
+
+@pytest.mark.parametrize("M,N,want", [
+    (4096, 4096, (1, 4096, 4096)),        # no remainder
+    (4096, 4097, (2, 4096, 4096)),        # 1-column sliver
+    (4096 + 64, 4096, (2, 4096, 4096)),   # 64-row sliver (<= 1/4 of 256)
+    (4096 + 65, 4096, (1, 4161, 4096)),   # 65 rows: more than a quarter, kept
+    (4096 + 3, 4096 + 5, (4, 4096, 4096)),  # right, bottom and corner strips
+    (1000, 1001, (1, 1000, 1001)),        # small: fewer than 128 full tiles, kept
+])
+def test_edge_split_plans(M, N, want):
+    p = plan(M, N, 512)
+    assert (p["launches"], p["main_m"], p["main_n"]) == want
+    assert plan(M, N, 512, split_edges=g.SPLIT_OFF)["launches"] == 1
+    # a forced tile splits only when asked
+    assert plan(M, N, 512, tile=g.TILE_256x256x64)["launches"] == 1
+    assert plan(M, N, 512, tile=g.TILE_256x256x64, split_edges=g.SPLIT_ON)["launches"] >= 1

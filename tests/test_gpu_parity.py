@@ -152,6 +152,21 @@ def test_ragged_equals_front_padded(tile):
     assert np.array_equal(C, Cp[:M, :N])
 
 
+@pytest.mark.parametrize("M,N", [(4095, 4097), (4096 + 3, 4096 + 5), (4096 + 64, 4096 + 1)])
+def test_edge_split_changes_no_bit(M, N):
+    """Splitting thin edge slivers into their own launches leaves every element unchanged."""
+    K = 1000
+    A, B = operands(M, N, K, "n(0,0.1)", M + N)
+    Ad, Bd = to_dev(A), to_dev(B)
+    rc, info = g.gemm_f16f32_plan(M, N, K, 1 << 40, 2 << 40, 3 << 40, K, N, N)
+    assert info["launches"] > 1
+    split = from_dev(run(Ad, Bd, M, N, K))
+    whole = from_dev(run(Ad, Bd, M, N, K, split_edges=g.SPLIT_OFF))
+    assert np.array_equal(split, whole)
+    r, c = sample_positions(M, N, 512, 512, 4, 5)
+    assert_within_tolerance(split[r, c], oracle.gemm_sampled(A, B, r, c), f"{M}x{N} split")
+
+
 def test_ragged_generic_path_within_tolerance():
     """The register-staged generic path on the ragged shape (its own k order)."""
     _, M, N, K, dist, seed = workload("gemm4095x4097x4093_n")
