@@ -55,7 +55,7 @@ def test_version_and_strerror():
     ((8, 8, 8, PA, PB, PA + 16, 8, 8, 8), g.ERR_OVERLAP),
     ((8, 8, 8, PA, PB, PB + 126, 8, 8, 8), g.ERR_OVERLAP),
     ((8, 8, 8, PA + 1, PB, PC, 8, 8, 8), g.ERR_OPTS),
-    ((8, 8, 8, PA, PB, PC, 1 << 24, 8, 8), g.ERR_TOO_LARGE),
+    ((8, 8, 8, 1 << 40, 2 << 40, 3 << 40, 1 << 26, 8, 8), g.ERR_TOO_LARGE),  # 64 x lda >= 2^31
 ])
 def test_argument_errors_before_launch(args, code):
     assert g.gemm_f16f32(*args, None) == code
