@@ -1,0 +1,41 @@
+"""Host-side behaviour of bench.py that needs no GPU."""
+import json
+import os
+import subprocess
+import sys
+
+import bench
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2 and "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_traffic_record_matches_current_kernel_source():
+    with open(bench.TRAFFIC_FILE) as f:
+        rec = json.load(f)
+    e = rec["gemm8192_u/tile1/g8/remap1"]
+    fetch = e["fetch_size_kib_per_dispatch"] * 1024 * e["fetch_factor"]
+    write = e["write_size_kib_per_dispatch"] * 1024 * e["write_factor"]
+    assert abs(fetch + write - e["bytes_per_launch"]) < 1e3
+    assert e["algorithmic_bytes_per_launch"] == 2 * 3 * 8192 * 8192
+    if e["source_hash"] == bench.kernel_source_hash():
+        assert bench.measured_traffic("gemm8192_u", 1, 8, 1) == e["bytes_per_launch"]
+    # any other launch configuration, or a changed kernel, reports no traffic
+    assert bench.measured_traffic("gemm8192_u", 1, 4, 1) is None
+    assert bench.measured_traffic("gemm4096_u", 1, 8, 1) is None
+
+
+def test_traffic_is_dropped_when_the_kernel_changes(tmp_path, monkeypatch):
+    rec = {"w/tile1/g8/remap1": {"source_hash": "0000", "bytes_per_launch": 5}}
+    p = tmp_path / "traffic.json"
+    p.write_text(json.dumps(rec))
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(p))
+    assert bench.measured_traffic("w", 1, 8, 1) is None
+    rec["w/tile1/g8/remap1"]["source_hash"] = bench.kernel_source_hash()
+    p.write_text(json.dumps(rec))
+    assert bench.measured_traffic("w", 1, 8, 1) == 5
