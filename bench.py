@@ -6,13 +6,16 @@ then K timed steps bracketed by device synchronisation.  Per-launch durations co
 HIP events recorded on the stream the kernel is launched on (torch's current stream).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--all]
-                    [--tile T] [--group-m G] [--xcd-remap R] [--no-cpu-baseline]
+                    [--tile T] [--group-m G] [--xcd-remap R] [--layout AB[C]]
+                    [--layouts] [--no-cpu-baseline]
 
 `value` is TFLOP/s = 2 M N K K_steps / (timed wall time); `roofline.achieved` is
 2 M N K / (mean per-launch event time), against the MI355X published dense fp16 matrix
 peak of 2.5 PFLOP/s.  `cpu_baseline` times the CPU oracle (fp64 ascending-k sums, one
 rounding) on one 256-row band of the same product, using all host threads it gets.
---all prints one extra JSON line per workload to stderr.
+--all prints one extra JSON line per workload to stderr.  --layout stores A, B (and C) row-
+major ("n") or column-major ("t"), e.g. "nt" for B given as an N x K matrix; --layouts times
+all eight storage orders (stderr).
 """
 from __future__ import annotations
 
@@ -74,13 +77,27 @@ def device_operands(torch, name):
     return _DEVICE_OPERANDS[name]
 
 
-def time_workload(g, torch, name, steps, warmup, opts):
+def layout_views(torch, A, B, C, layout):
+    """A, B, C as views with the storage orders named by `layout` ("n" row-major, "t"
+    column-major, for A, B and optionally C; the data are the same logical matrices)."""
+    lay = (layout + "n")[:3]
+    if lay[0] == "t":
+        A = A.t().contiguous().t()
+    if lay[1] == "t":
+        B = B.t().contiguous().t()
+    if lay[2] == "t":
+        C = torch.empty((C.shape[1], C.shape[0]), dtype=C.dtype, device=C.device).t()
+    return A, B, C
+
+
+def time_workload(g, torch, name, steps, warmup, opts, layout="nn"):
     from synthetic_inputs import workload
 
     _, M, N, K, _, _ = workload(name)
-    Ad, Bd, Cd = device_operands(torch, name)
-    rc, plan = g.gemm_f16f32_plan(M, N, K, Ad.data_ptr(), Bd.data_ptr(), Cd.data_ptr(), K, N, N,
-                                  opts=opts or None)
+    Ad, Bd, Cd = layout_views(torch, *device_operands(torch, name), layout)
+    rc, plan = g.gemm_f16f32_strided_plan(M, N, K, Ad.data_ptr(), *Ad.stride(), Bd.data_ptr(),
+                                          *Bd.stride(), Cd.data_ptr(), *Cd.stride(),
+                                          opts=opts or None)
     if rc != g.OK:
         raise g.GemmError(rc, "plan")
     stream = torch.cuda.current_stream()
@@ -101,7 +118,7 @@ def time_workload(g, torch, name, steps, warmup, opts):
     flops = 2.0 * M * N * K
     mean_ms = sum(per) / len(per)
     return {
-        "workload": name, "M": M, "N": N, "K": K, "plan": plan,
+        "workload": name, "M": M, "N": N, "K": K, "layout": layout, "plan": plan,
         "value": flops * steps / wall / 1e12, "ms_per_step": wall * 1e3 / steps,
         "kernel_ms_mean": mean_ms, "kernel_ms_median": per[len(per) // 2],
         "kernel_ms_min": per[0], "kernel_ms_p90": per[min(len(per) - 1, int(0.9 * len(per)))],
@@ -180,6 +197,10 @@ def main():
     ap.add_argument("--group-m", type=int, default=0)
     ap.add_argument("--xcd-remap", type=int, default=0)
     ap.add_argument("--force-generic", type=int, default=0)
+    ap.add_argument("--layout", default="nn",
+                    help="storage of A, B[, C]: n = row-major, t = column-major (e.g. nt)")
+    ap.add_argument("--layouts", action="store_true",
+                    help="time every storage order of A, B and C (stderr)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sweep", action="store_true",
                     help="time GROUP_SIZE_M in 1..32 with the XCD permutation on and off (stderr)")
@@ -223,13 +244,21 @@ def main():
                                   "tflops": round(rr["achieved_tflops"], 1),
                                   "kernel_ms_median": round(rr["kernel_ms_median"], 4)}),
                       file=sys.stderr, flush=True)
+    if args.layouts:
+        for lay in ("nn", "nt", "tn", "tt", "nnt", "ntt", "tnt", "ttt"):
+            rr = time_workload(g, torch, args.workload, args.steps, args.warmup, opts, lay)
+            print(json.dumps({"workload": args.workload, "layout": lay,
+                              "tflops": round(rr["achieved_tflops"], 1),
+                              "kernel_ms_median": round(rr["kernel_ms_median"], 4)}),
+                  file=sys.stderr, flush=True)
     if args.torch:
         print(json.dumps(time_torch(torch, args.workload, args.steps, args.warmup)),
               file=sys.stderr, flush=True)
 
-    r = time_workload(g, torch, args.workload, args.steps, args.warmup, opts)
+    r = time_workload(g, torch, args.workload, args.steps, args.warmup, opts, args.layout)
     plan = r["plan"]
-    traffic = measured_traffic(args.workload, plan["tile"], plan["group_m"], plan["xcd_remap"])
+    traffic = (measured_traffic(args.workload, plan["tile"], plan["group_m"], plan["xcd_remap"])
+               if args.layout == "nn" else None)
     out = {
         "metric": METRIC,
         "value": round(r["value"], 2),
@@ -245,7 +274,8 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": args.workload, "M": r["M"], "N": r["N"], "K": r["K"],
-            "accumulate": "f32", "path": ["dma", "generic"][plan["path"]],
+            "accumulate": "f32", "layout": args.layout,
+            "path": ["dma", "generic"][plan["path"]],
             "tile": f"{plan['bm']}x{plan['bn']}x{plan['bk']}", "group_m": plan["group_m"],
             "xcd_remap": plan["xcd_remap"], "workgroups": plan["num_programs"],
         },

@@ -1,10 +1,11 @@
 """Python binding of libgemm_f16f32.so (the gfx950 fp16/fp32-accumulate GEMM).
 
 The functions named like the C-ABI (gemm_f16f32, gemm_f16f32_ex, gemm_f16f32_plan,
-gemm_f16f32_tile_map, gemm_f16f32_strerror, gemm_f16f32_version) only marshal arguments
-into the library; every step of the computation runs in its HIP kernels.  `matmul` is the
-same call for torch tensors: it passes their device pointers, leading dimensions and
-torch's current HIP stream.  PyTorch is used for device memory and streams only.
+gemm_f16f32_strided, gemm_f16f32_strided_plan, gemm_f16f32_tile_map, gemm_f16f32_strerror,
+gemm_f16f32_version) only marshal arguments into the library; every step of the computation
+runs in its HIP kernels.  `matmul` is the same call for torch tensors: it passes their device
+pointers, element strides (row- or column-major, any leading dimension) and torch's current
+HIP stream.  PyTorch is used for device memory and streams only.
 
 The library is loaded on first use; if it has not been built the call raises at once
 (there is no fallback of any kind).
@@ -44,7 +45,8 @@ class Opts(ctypes.Structure):
 class PlanInfo(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in ("path", "tile", "bm", "bn", "bk", "group_m",
                                               "xcd_remap", "num_pid_m", "num_pid_n",
-                                              "num_programs", "launches", "main_m", "main_n")]
+                                              "num_programs", "launches", "main_m", "main_n",
+                                              "a_kmajor", "b_kmajor", "swapped")]
 
     def as_dict(self) -> dict:
         return {n: getattr(self, n) for n, _ in self._fields_}
@@ -54,6 +56,7 @@ _lib = None
 _i64 = ctypes.c_int64
 _vp = ctypes.c_void_p
 _GEMM_ARGS = [_i64, _i64, _i64, _vp, _vp, _vp, _i64, _i64, _i64]
+_STRIDED_ARGS = [_i64, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _i64]
 
 
 def lib() -> ctypes.CDLL:
@@ -71,6 +74,11 @@ def lib() -> ctypes.CDLL:
         L.gemm_f16f32_plan.argtypes = _GEMM_ARGS + [ctypes.POINTER(Opts),
                                                     ctypes.POINTER(PlanInfo)]
         L.gemm_f16f32_plan.restype = ctypes.c_int
+        L.gemm_f16f32_strided.argtypes = _STRIDED_ARGS + [_vp, ctypes.POINTER(Opts)]
+        L.gemm_f16f32_strided.restype = ctypes.c_int
+        L.gemm_f16f32_strided_plan.argtypes = _STRIDED_ARGS + [ctypes.POINTER(Opts),
+                                                               ctypes.POINTER(PlanInfo)]
+        L.gemm_f16f32_strided_plan.restype = ctypes.c_int
         L.gemm_f16f32_tile_map.argtypes = [ctypes.c_int32] * 4 + [_vp, _vp]
         L.gemm_f16f32_tile_map.restype = ctypes.c_int
         L.gemm_f16f32_strerror.argtypes = [ctypes.c_int]
@@ -108,6 +116,26 @@ def gemm_f16f32_plan(M, N, K, A, B, C, lda, ldb, ldc, opts=None):
     return rc, (info.as_dict() if rc == OK else None)
 
 
+def gemm_f16f32_strided(M, N, K, A, stride_am, stride_ak, B, stride_bk, stride_bn, C,
+                        stride_cm, stride_cn, stream=None, opts=None) -> int:
+    o = _opts(opts)
+    return lib().gemm_f16f32_strided(M, N, K, A, stride_am, stride_ak, B, stride_bk, stride_bn,
+                                     C, stride_cm, stride_cn, stream,
+                                     ctypes.byref(o) if o is not None else None)
+
+
+def gemm_f16f32_strided_plan(M, N, K, A, stride_am, stride_ak, B, stride_bk, stride_bn, C,
+                             stride_cm, stride_cn, opts=None):
+    """(code, dict of the plan) -- host only, nothing is launched."""
+    o = _opts(opts)
+    info = PlanInfo()
+    rc = lib().gemm_f16f32_strided_plan(M, N, K, A, stride_am, stride_ak, B, stride_bk,
+                                        stride_bn, C, stride_cm, stride_cn,
+                                        ctypes.byref(o) if o is not None else None,
+                                        ctypes.byref(info))
+    return rc, (info.as_dict() if rc == OK else None)
+
+
 def gemm_f16f32_tile_map(num_pid_m, num_pid_n, group_m, xcd_remap, out_dev, stream=None) -> int:
     return lib().gemm_f16f32_tile_map(num_pid_m, num_pid_n, group_m, xcd_remap, out_dev, stream)
 
@@ -122,14 +150,6 @@ def gemm_f16f32_version() -> int:
 
 # ---- torch tensors -------------------------------------------------------------------------
 
-def _ld(t) -> int:
-    if t.dim() != 2:
-        raise ValueError("expected a 2-D tensor")
-    if t.numel() and t.stride(1) != 1:
-        raise ValueError("expected unit stride along rows")
-    return max(t.stride(0), t.shape[1], 1)
-
-
 def _stream_handle(stream):
     import torch
     s = torch.cuda.current_stream() if stream is None else stream
@@ -140,9 +160,10 @@ def matmul(a, b, out=None, *, M=None, N=None, K=None, stream=None, **opts):
     """out[:M, :N] = fp16(a[:M, :K] @ b[:K, :N]) on the GPU (fp32 accumulation).
 
     a, b, out: 2-D CUDA tensors of 16-bit elements (float16, or int16 holding fp16 bits),
-    row-major with unit inner stride and any leading dimension.  opts: tile, group_m,
-    xcd_remap, force_generic, split_edges (see include/gemm_f16f32.h).  Raises GemmError on a non-zero
-    return code.  Launches on torch's current stream unless `stream` is given.
+    each row-major or column-major (one unit stride) with any leading dimension: transposed
+    views such as `w.t()` are read in place.  opts: tile, group_m, xcd_remap, force_generic,
+    split_edges (see include/gemm_f16f32.h).  Raises GemmError on a non-zero return code.
+    Launches on torch's current stream unless `stream` is given.
     """
     import torch
     M = a.shape[0] if M is None else M
@@ -151,12 +172,16 @@ def matmul(a, b, out=None, *, M=None, N=None, K=None, stream=None, **opts):
     if out is None:
         out = torch.empty((M, N), dtype=a.dtype, device=a.device)
     for t in (a, b, out):
+        if t.dim() != 2:
+            raise ValueError("expected 2-D tensors")
         if t.element_size() != 2 or not t.is_cuda:
             raise ValueError("operands must be 16-bit CUDA tensors")
-    rc = gemm_f16f32_ex(M, N, K, a.data_ptr(), b.data_ptr(), out.data_ptr(), _ld(a), _ld(b),
-                        _ld(out), _stream_handle(stream), Opts(**opts) if opts else None)
+    rc = gemm_f16f32_strided(M, N, K, a.data_ptr(), a.stride(0), a.stride(1), b.data_ptr(),
+                             b.stride(0), b.stride(1), out.data_ptr(), out.stride(0),
+                             out.stride(1), _stream_handle(stream),
+                             Opts(**opts) if opts else None)
     if rc != OK:
-        raise GemmError(rc, "gemm_f16f32_ex")
+        raise GemmError(rc, "gemm_f16f32_strided")
     return out
 
 

@@ -9,7 +9,7 @@
 
 namespace {
 
-constexpr int kVersion = 100;  // 0.1.0
+constexpr int kVersion = 200;  // 0.2.0
 
 // bk: panel depth of the DMA kernel (the generic kernel always uses 64-deep panels);
 // stages: LDS stages of the DMA kernel.
@@ -60,6 +60,51 @@ bool overlaps(const void* a, uint64_t na, const void* b, uint64_t nb) {
   return x < y + nb && y < x + na;
 }
 
+// A problem as the kernels see it: C (M x N, row-major, ldc) = A (M x K) B (K x N), each
+// operand either k-major (consecutive k adjacent: A[i][k] at A + i*lda + k, B[k][j] at
+// B + j*ldb + k) or x-major (A[i][k] at A + k*lda + i, B[k][j] at B + k*ldb + j).
+// `swapped`: the caller's C is column-major and this is its transpose, C^T = B^T A^T.
+struct Problem {
+  int64_t M, N, K;
+  const uint16_t* A;
+  const uint16_t* B;
+  const uint16_t* C;
+  int64_t lda, ldb, ldc;
+  bool a_kmajor, b_kmajor, swapped;
+};
+
+// Storage order of an R x S matrix with element strides sr (between rows) and sc (between
+// columns): 0 = row-major (sc == 1, ld = sr >= S), 1 = column-major (sr == 1, ld = sc >= R),
+// -1 = neither.  The stride along an axis of extent 1 is never used and is ignored; an empty
+// matrix is never addressed and counts as row-major.
+int order_of(int64_t R, int64_t S, int64_t sr, int64_t sc, int64_t* ld) {
+  if (R == 0 || S == 0 || (R == 1 && S == 1)) {
+    *ld = S > 1 ? S : 1;
+    return 0;
+  }
+  if (R == 1) {  // one row: only sc is used
+    if (sc == 1) {
+      *ld = S;
+      return 0;
+    }
+    *ld = sc;
+    return sc >= 1 ? 1 : -1;
+  }
+  if (S == 1) {  // one column: only sr is used
+    *ld = sr;
+    return sr >= 1 ? 0 : -1;
+  }
+  if (sc == 1 && sr >= S) {
+    *ld = sr;
+    return 0;
+  }
+  if (sr == 1 && sc >= R) {
+    *ld = sc;
+    return 1;
+  }
+  return -1;
+}
+
 // One launch over an M x N block of C (all of it, or one part of an edge split).
 struct Part {
   int64_t m_off, n_off, M, N;
@@ -67,11 +112,13 @@ struct Part {
 };
 
 // Fills r for one launch of tile `tile` over M x N (no argument checks here).
-int plan_launch(int64_t M, int64_t N, int64_t lda, int64_t ldb, const TileDesc* t,
+int plan_launch(const Problem& pr, int64_t M, int64_t N, const TileDesc* t,
                 const gemm_f16f32_opts& o, gemm_f16f32_plan_info* r) {
   const int64_t kMax = (int64_t)1 << 31;
-  // 32-bit in-kernel offsets: one panel's rows of A (bm x lda) and of B (64 x ldb).
-  if ((int64_t)t->bm * lda >= kMax || (int64_t)gk::kBK * ldb >= kMax)
+  // 32-bit in-kernel offsets: one panel's stored rows of A (bm rows if k-major, else up to 64
+  // k rows) and of B (bn or 64), and one tile's bm rows of C.
+  const int64_t rows_a = pr.a_kmajor ? t->bm : gk::kBK, rows_b = pr.b_kmajor ? t->bn : gk::kBK;
+  if (rows_a * pr.lda >= kMax || rows_b * pr.ldb >= kMax || (int64_t)t->bm * pr.ldc >= kMax)
     return GEMM_F16F32_ERR_TOO_LARGE;
   const bool dma = !o.force_generic;
   r->path = dma ? GEMM_F16F32_PATH_DMA : GEMM_F16F32_PATH_GENERIC;
@@ -90,6 +137,9 @@ int plan_launch(int64_t M, int64_t N, int64_t lda, int64_t ldb, const TileDesc* 
   r->launches = empty ? 0 : 1;
   r->main_m = (int32_t)M;
   r->main_n = (int32_t)N;
+  r->a_kmajor = pr.a_kmajor;
+  r->b_kmajor = pr.b_kmajor;
+  r->swapped = pr.swapped;
   return GEMM_F16F32_OK;
 }
 
@@ -103,18 +153,19 @@ int plan_launch(int64_t M, int64_t N, int64_t lda, int64_t ldb, const TileDesc* 
 // sliver is then computed by separate launches with tiles chosen for its own shape.  Every
 // element's k-sum is the same sequence of MFMA steps whatever the tile, so results do not
 // change.
-int plan_parts(int64_t M, int64_t N, int64_t K, const uint16_t* A, const uint16_t* B,
-               const uint16_t* C, int64_t lda, int64_t ldb, int64_t ldc,
-               const gemm_f16f32_opts* opts, Part* parts, int* nparts) {
+int plan_parts(const Problem& pr, const gemm_f16f32_opts* opts, Part* parts, int* nparts) {
   const int64_t kMax = (int64_t)1 << 31;
+  const int64_t M = pr.M, N = pr.N, K = pr.K;
   *nparts = 0;
   if (M < 0 || N < 0 || K < 0 || M >= kMax || N >= kMax || K >= kMax) return GEMM_F16F32_ERR_DIM;
-  if (lda < (K > 1 ? K : 1) || ldb < (N > 1 ? N : 1) || ldc < (N > 1 ? N : 1))
+  const int64_t min_lda = pr.a_kmajor ? K : M, min_ldb = pr.b_kmajor ? K : N;
+  if (pr.lda < (min_lda > 1 ? min_lda : 1) || pr.ldb < (min_ldb > 1 ? min_ldb : 1) ||
+      pr.ldc < (N > 1 ? N : 1))
     return GEMM_F16F32_ERR_LD;
   const bool emptyC = (M == 0 || N == 0);
-  if (!emptyC && C == nullptr) return GEMM_F16F32_ERR_NULL;
-  if (!emptyC && K > 0 && (A == nullptr || B == nullptr)) return GEMM_F16F32_ERR_NULL;
-  if (((uintptr_t)A | (uintptr_t)B | (uintptr_t)C) & 1) return GEMM_F16F32_ERR_OPTS;
+  if (!emptyC && pr.C == nullptr) return GEMM_F16F32_ERR_NULL;
+  if (!emptyC && K > 0 && (pr.A == nullptr || pr.B == nullptr)) return GEMM_F16F32_ERR_NULL;
+  if (((uintptr_t)pr.A | (uintptr_t)pr.B | (uintptr_t)pr.C) & 1) return GEMM_F16F32_ERR_OPTS;
 
   gemm_f16f32_opts o = {0, 0, 0, 0, 0};
   if (opts) o = *opts;
@@ -124,8 +175,10 @@ int plan_parts(int64_t M, int64_t N, int64_t K, const uint16_t* A, const uint16_
     return GEMM_F16F32_ERR_OPTS;
 
   if (!emptyC) {
-    const uint64_t fc = footprint(M, N, ldc);
-    if (overlaps(C, fc, A, footprint(M, K, lda)) || overlaps(C, fc, B, footprint(K, N, ldb)))
+    const uint64_t fc = footprint(M, N, pr.ldc);
+    const uint64_t fa = pr.a_kmajor ? footprint(M, K, pr.lda) : footprint(K, M, pr.lda);
+    const uint64_t fb = pr.b_kmajor ? footprint(N, K, pr.ldb) : footprint(K, N, pr.ldb);
+    if (overlaps(pr.C, fc, pr.A, fa) || overlaps(pr.C, fc, pr.B, fb))
       return GEMM_F16F32_ERR_OVERLAP;
   }
 
@@ -142,7 +195,7 @@ int plan_parts(int64_t M, int64_t N, int64_t K, const uint16_t* A, const uint16_
   }
   Part* pp = parts;
   pp->m_off = 0, pp->n_off = 0, pp->M = Mm, pp->N = Nm;
-  int rc = plan_launch(Mm, Nm, lda, ldb, t, o, &pp->r);
+  int rc = plan_launch(pr, Mm, Nm, t, o, &pp->r);
   if (rc != GEMM_F16F32_OK) return rc;
   ++pp;
   const int64_t strips[3][4] = {{0, Nm, Mm, N - Nm}, {Mm, 0, M - Mm, Nm}, {Mm, Nm, M - Mm, N - Nm}};
@@ -152,7 +205,7 @@ int plan_parts(int64_t M, int64_t N, int64_t K, const uint16_t* A, const uint16_
   for (const auto& st : strips) {
     if (st[2] == 0 || st[3] == 0) continue;
     pp->m_off = st[0], pp->n_off = st[1], pp->M = st[2], pp->N = st[3];
-    rc = plan_launch(st[2], st[3], lda, ldb, find_tile(auto_tile(st[2], st[3])), os, &pp->r);
+    rc = plan_launch(pr, st[2], st[3], find_tile(auto_tile(st[2], st[3])), os, &pp->r);
     if (rc != GEMM_F16F32_OK) return rc;
     ++pp;
   }
@@ -161,39 +214,48 @@ int plan_parts(int64_t M, int64_t N, int64_t K, const uint16_t* A, const uint16_
   return GEMM_F16F32_OK;
 }
 
-template <int BM, int BN, int BK, int NS>
-hipError_t launch(const gemm_f16f32_plan_info& r, const gk::Args& a, bool odd,
-                  hipStream_t stream) {
+template <int BM, int BN, int BK, int NS, bool AKM, bool BKM>
+hipError_t launch_layout(const gemm_f16f32_plan_info& r, const gk::Args& a, bool odd,
+                         hipStream_t stream) {
   const dim3 grid(r.num_programs), block(gk::kThreads);
   if (r.path == GEMM_F16F32_PATH_DMA)
-    hipLaunchKernelGGL((gk::gemm_dma<BM, BN, BK, NS>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((gk::gemm_dma<BM, BN, BK, NS, AKM, BKM>), grid, block, 0, stream, a);
   else if (odd)
-    hipLaunchKernelGGL((gk::gemm_generic<BM, BN, true>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((gk::gemm_generic<BM, BN, true, AKM, BKM>), grid, block, 0, stream, a);
   else
-    hipLaunchKernelGGL((gk::gemm_generic<BM, BN, false>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((gk::gemm_generic<BM, BN, false, AKM, BKM>), grid, block, 0, stream, a);
   return hipGetLastError();
 }
 
-int launch_part(const Part& pt, int64_t K, const uint16_t* A, const uint16_t* B, uint16_t* C,
-                int64_t lda, int64_t ldb, int64_t ldc, hipStream_t s) {
+template <int BM, int BN, int BK, int NS>
+hipError_t launch(const gemm_f16f32_plan_info& r, const gk::Args& a, bool odd,
+                  hipStream_t stream) {
+  if (r.a_kmajor)
+    return r.b_kmajor ? launch_layout<BM, BN, BK, NS, true, true>(r, a, odd, stream)
+                      : launch_layout<BM, BN, BK, NS, true, false>(r, a, odd, stream);
+  return r.b_kmajor ? launch_layout<BM, BN, BK, NS, false, true>(r, a, odd, stream)
+                    : launch_layout<BM, BN, BK, NS, false, false>(r, a, odd, stream);
+}
+
+int launch_part(const Problem& pr, const Part& pt, hipStream_t s) {
   const gemm_f16f32_plan_info& r = pt.r;
   if (r.num_programs == 0) return GEMM_F16F32_OK;
   gk::Args a;
-  a.A = A + pt.m_off * lda;
-  a.B = B + pt.n_off;
-  a.C = C + pt.m_off * ldc + pt.n_off;
-  a.lda = lda;
-  a.ldb = ldb;
-  a.ldc = ldc;
+  a.A = pr.A + (pr.a_kmajor ? pt.m_off * pr.lda : pt.m_off);
+  a.B = pr.B + (pr.b_kmajor ? pt.n_off * pr.ldb : pt.n_off);
+  a.C = const_cast<uint16_t*>(pr.C) + pt.m_off * pr.ldc + pt.n_off;
+  a.lda = pr.lda;
+  a.ldb = pr.ldb;
+  a.ldc = pr.ldc;
   a.M = (int32_t)pt.M;
   a.N = (int32_t)pt.N;
-  a.K = (int32_t)K;
+  a.K = (int32_t)pr.K;
   a.num_pid_m = r.num_pid_m;
   a.num_pid_n = r.num_pid_n;
   a.group_m = r.group_m;
   a.xcd_remap = r.xcd_remap;
   a.num_programs = r.num_programs;
-  const bool odd = (((uintptr_t)a.A | (uintptr_t)a.B) & 3) != 0 || ((lda | ldb) & 1) != 0;
+  const bool odd = (((uintptr_t)a.A | (uintptr_t)a.B) & 3) != 0 || ((pr.lda | pr.ldb) & 1) != 0;
   hipError_t e = hipSuccess;
   switch (r.tile) {
     case GEMM_F16F32_TILE_256x256x64: e = launch<256, 256, 64, 2>(r, a, odd, s); break;
@@ -208,6 +270,48 @@ int launch_part(const Part& pt, int64_t K, const uint16_t* A, const uint16_t* B,
   return e == hipSuccess ? GEMM_F16F32_OK : GEMM_F16F32_ERR_HIP;
 }
 
+Problem row_major_problem(int64_t M, int64_t N, int64_t K, const uint16_t* A, const uint16_t* B,
+                          const uint16_t* C, int64_t lda, int64_t ldb, int64_t ldc) {
+  return Problem{M, N, K, A, B, C, lda, ldb, ldc, true, false, false};
+}
+
+// Problem for caller strides (A: sam, sak; B: sbk, sbn; C: scm, scn).  A column-major C is
+// turned into its transpose, C^T = B^T A^T, with the operands' roles exchanged: B^T is k-major
+// exactly when B is stored column-major, and A^T exactly when A is stored row-major.
+int strided_problem(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t sam,
+                    int64_t sak, const uint16_t* B, int64_t sbk, int64_t sbn, const uint16_t* C,
+                    int64_t scm, int64_t scn, Problem* pr) {
+  const int64_t kMax = (int64_t)1 << 31;
+  if (M < 0 || N < 0 || K < 0 || M >= kMax || N >= kMax || K >= kMax) return GEMM_F16F32_ERR_DIM;
+  int64_t lda = 0, ldb = 0, ldc = 0;
+  const int oa = order_of(M, K, sam, sak, &lda);
+  const int ob = order_of(K, N, sbk, sbn, &ldb);
+  const int oc = order_of(M, N, scm, scn, &ldc);
+  if (oa < 0 || ob < 0 || oc < 0) return GEMM_F16F32_ERR_LD;
+  if (oc == 0)
+    *pr = Problem{M, N, K, A, B, C, lda, ldb, ldc, oa == 0, ob == 1, false};
+  else
+    *pr = Problem{N, M, K, B, A, C, ldb, lda, ldc, ob == 1, oa == 0, true};
+  return GEMM_F16F32_OK;
+}
+
+int run(const Problem& pr, void* stream, const gemm_f16f32_opts* opts) {
+  Part parts[4];
+  int n = 0;
+  int rc = plan_parts(pr, opts, parts, &n);
+  for (int i = 0; i < n && rc == GEMM_F16F32_OK; ++i)
+    rc = launch_part(pr, parts[i], (hipStream_t)stream);
+  return rc;
+}
+
+int plan(const Problem& pr, const gemm_f16f32_opts* opts, gemm_f16f32_plan_info* info) {
+  Part parts[4];
+  int n = 0;
+  const int rc = plan_parts(pr, opts, parts, &n);
+  if (rc == GEMM_F16F32_OK && info) *info = parts[0].r;
+  return rc;
+}
+
 }  // namespace
 
 extern "C" {
@@ -215,28 +319,39 @@ extern "C" {
 int gemm_f16f32_plan(int64_t M, int64_t N, int64_t K, const uint16_t* A, const uint16_t* B,
                      const uint16_t* C, int64_t lda, int64_t ldb, int64_t ldc,
                      const gemm_f16f32_opts* opts, gemm_f16f32_plan_info* info) {
-  Part parts[4];
-  int n = 0;
-  const int rc = plan_parts(M, N, K, A, B, C, lda, ldb, ldc, opts, parts, &n);
-  if (rc == GEMM_F16F32_OK && info) *info = parts[0].r;
-  return rc;
+  return plan(row_major_problem(M, N, K, A, B, C, lda, ldb, ldc), opts, info);
 }
 
 int gemm_f16f32_ex(int64_t M, int64_t N, int64_t K, const uint16_t* A, const uint16_t* B,
                    uint16_t* C, int64_t lda, int64_t ldb, int64_t ldc, void* stream,
                    const gemm_f16f32_opts* opts) {
-  Part parts[4];
-  int n = 0;
-  int rc = plan_parts(M, N, K, A, B, C, lda, ldb, ldc, opts, parts, &n);
-  if (rc != GEMM_F16F32_OK) return rc;
-  for (int i = 0; i < n && rc == GEMM_F16F32_OK; ++i)
-    rc = launch_part(parts[i], K, A, B, C, lda, ldb, ldc, (hipStream_t)stream);
-  return rc;
+  return run(row_major_problem(M, N, K, A, B, C, lda, ldb, ldc), stream, opts);
 }
 
 int gemm_f16f32(int64_t M, int64_t N, int64_t K, const uint16_t* A, const uint16_t* B,
                 uint16_t* C, int64_t lda, int64_t ldb, int64_t ldc, void* stream) {
   return gemm_f16f32_ex(M, N, K, A, B, C, lda, ldb, ldc, stream, nullptr);
+}
+
+int gemm_f16f32_strided(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t stride_am,
+                        int64_t stride_ak, const uint16_t* B, int64_t stride_bk,
+                        int64_t stride_bn, uint16_t* C, int64_t stride_cm, int64_t stride_cn,
+                        void* stream, const gemm_f16f32_opts* opts) {
+  Problem pr;
+  const int rc = strided_problem(M, N, K, A, stride_am, stride_ak, B, stride_bk, stride_bn, C,
+                                 stride_cm, stride_cn, &pr);
+  return rc != GEMM_F16F32_OK ? rc : run(pr, stream, opts);
+}
+
+int gemm_f16f32_strided_plan(int64_t M, int64_t N, int64_t K, const uint16_t* A,
+                             int64_t stride_am, int64_t stride_ak, const uint16_t* B,
+                             int64_t stride_bk, int64_t stride_bn, const uint16_t* C,
+                             int64_t stride_cm, int64_t stride_cn, const gemm_f16f32_opts* opts,
+                             gemm_f16f32_plan_info* info) {
+  Problem pr;
+  const int rc = strided_problem(M, N, K, A, stride_am, stride_ak, B, stride_bk, stride_bn, C,
+                                 stride_cm, stride_cn, &pr);
+  return rc != GEMM_F16F32_OK ? rc : plan(pr, opts, info);
 }
 
 int gemm_f16f32_tile_map(int32_t num_pid_m, int32_t num_pid_n, int32_t group_m,
@@ -256,7 +371,7 @@ const char* gemm_f16f32_strerror(int code) {
     case GEMM_F16F32_OK: return "success";
     case GEMM_F16F32_ERR_DIM: return "M, N or K negative or too large";
     case GEMM_F16F32_ERR_NULL: return "NULL pointer for a non-empty operand";
-    case GEMM_F16F32_ERR_LD: return "leading dimension smaller than the row length";
+    case GEMM_F16F32_ERR_LD: return "unsupported strides: leading dimension too small or no unit stride";
     case GEMM_F16F32_ERR_OVERLAP: return "C overlaps A or B";
     case GEMM_F16F32_ERR_OPTS: return "invalid option or misaligned pointer";
     case GEMM_F16F32_ERR_TOO_LARGE: return "leading dimension too large for 32-bit tile offsets";

@@ -73,29 +73,65 @@ __device__ __forceinline__ void program_tile(int h, int P, int num_pid_m, int nu
 }
 
 // ---------------------------------------------------------------------------------------
-// Tile geometry.
+// Operands.  Both MFMA operands have the same register shape: lane l holds the 8 k values
+// 8(l/32) .. 8(l/32)+7 at position l % 32 along the operand's other axis X (the row of A, the
+// column of B).  They differ only in how the matrix is stored:
+//  * k-major (KM): consecutive k are adjacent in memory -- A row-major (M x K), or B stored
+//    transposed (N x K).  Element (x, k) is at x * ld + k.
+//  * x-major: consecutive x are adjacent -- B row-major (K x N), or A stored transposed
+//    (K x M).  Element (x, k) is at k * ld + x.
+// An LDS panel keeps the operand's memory layout, in rows of 16-byte chunks:
+//  * k-major: BX rows of BK halves; one MFMA operand is one 16-byte read per lane;
+//  * x-major: BK rows of BX halves; one MFMA operand is two transposing reads per lane
+//    (ds_read_b64_tr_b16, 4 k rows each).
+// Chunk c of LDS row r sits at chunk position c ^ swz(r).
 // ---------------------------------------------------------------------------------------
-template <int BM_, int BN_, int BK_ = kBK>
-struct Tile {
-  static constexpr int BM = BM_, BN = BN_, BK = BK_;
-  static constexpr int WTM = BM / 2, WTN = BN / 2;   // per-wave block of C
-  static constexpr int TM = WTM / 32, TN = WTN / 32; // 32x32 MFMA blocks per wave
-  static constexpr int CA = BK / 8;                  // 16-byte chunks per LDS row of A
-  static constexpr int CB = BN / 8;                  // 16-byte chunks per LDS row of B
-  static constexpr int A_BYTES = BM * BK * 2;
-  static constexpr int B_BYTES = BK * BN * 2;
-  static constexpr int STAGE = A_BYTES + B_BYTES;
-  static constexpr int A_LD = A_BYTES / (kThreads * 16);  // 16-byte loads per thread
-  static constexpr int B_LD = B_BYTES / (kThreads * 16);
-  static_assert(TM >= 1 && TN >= 1 && (CA == 8 || CA == 4), "tile shape");
-  static_assert(A_LD >= 1 && B_LD >= 1, "tile too small for 256 threads");
+template <int BX_, int BK_, bool KM_>
+struct Opnd {
+  static constexpr int BX = BX_, BK = BK_;
+  static constexpr bool KM = KM_;
+  static constexpr int ROWS = KM ? BX : BK;          // LDS rows of one panel
+  static constexpr int CH = (KM ? BK : BX) / 8;      // 16-byte chunks per LDS row
+  static constexpr int ROW_BYTES = CH * 16;
+  static constexpr int BYTES = BX * BK * 2;
+  static constexpr int LD = BYTES / (kThreads * 16); // 16-byte loads per thread per panel
+  static constexpr int WX = BX / 2;                  // extent of one wave's block along X
+  static constexpr int T = WX / 32;                  // 32-wide MFMA blocks per wave
+  static constexpr int NOFF = KM ? BK / 16 : T;      // per-lane LDS read offsets
+  static constexpr int READS = KM ? T : 2 * T;       // LDS read instructions per k step
+  static_assert(T >= 1 && LD >= 1, "operand tile too small for 256 threads");
+  static_assert(!KM || CH == 8 || CH == 4, "k-major LDS rows hold 64 or 32 halves");
+  static_assert(KM || CH == 8 || CH == 16 || CH == 32, "x-major LDS rows hold 64-256 halves");
 };
+
+template <int BM_, int BN_, int BK_, bool AKM, bool BKM>
+struct Tile {
+  using OA = Opnd<BM_, BK_, AKM>;
+  using OB = Opnd<BN_, BK_, BKM>;
+  static constexpr int BM = BM_, BN = BN_, BK = BK_;
+  static constexpr int WTM = BM / 2, WTN = BN / 2;   // per-wave block of C (2 x 2 waves)
+  static constexpr int TM = OA::T, TN = OB::T;       // 32x32 MFMA blocks per wave
+  static constexpr int A_BYTES = OA::BYTES, B_BYTES = OB::BYTES;
+  static constexpr int STAGE = A_BYTES + B_BYTES;
+  static constexpr int A_LD = OA::LD, B_LD = OB::LD;
+};
+
+// Element offset of (x, k) inside an operand stored with leading dimension ld, and the
+// extent (elements from the first element to one past the last, (X-1, K-1)).
+template <bool KM>
+__device__ __forceinline__ int64_t elem_off(int64_t x, int64_t k, int64_t ld) {
+  return KM ? x * ld + k : k * ld + x;
+}
+template <bool KM>
+__device__ __forceinline__ int64_t extent(int64_t X, int64_t K, int64_t ld) {
+  return KM ? (X - 1) * ld + K : (K - 1) * ld + X;
+}
 
 // The hardware range-checks each dword of a buffer load on its own and returns 0 for a dword
 // that reaches past num_records, even partly.  The extent is therefore rounded up to whole
 // dwords: a matrix whose last element ends 2 bytes into a dword still gets that element.  The
 // 2 extra bytes share a dword (hence a page) with valid data, and they only ever land in
-// slots that are masked (k >= K) or never stored (columns >= N).
+// slots that are masked (k >= K) or never stored (rows >= M, columns >= N).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
   // Saturate to [0, 2^32 - 4] with 32-bit scalar operations only (no 64-bit compares, which
   // the scalar unit lacks and would move to the vector unit).
@@ -115,40 +151,36 @@ __device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t r, void
 #endif
 }
 
-// LDS layouts.  A panel: BM rows of BK halves (CA = BK/8 chunks of 16 B); chunk c of row r is
-// stored at chunk position c ^ swz_a(r).  An MFMA A-operand read has 32 lanes on 32
-// consecutive rows at one logical chunk; the hardware serves such a read 8 lanes (128 B) or
-// 16 lanes (256 B) at a time, so any 8 (and any 16) consecutive rows must land on distinct
-// bank groups:
-//  * 128-byte rows (BK = 64): swz = (r mod 8) xor bit 3 of r -- 8 rows give 8 distinct chunk
-//    positions, 16 rows 16 distinct (row parity, position) pairs;
-//  * 64-byte rows (BK = 32): two rows share a bank line; swz = (bits 1-2 of r) xor (bits 3-4)
-//    gives distinct (r mod 2, position) over 8 rows and distinct (r mod 4, position) over 16.
-// Both depend on r mod 32 only, so rows 32 apart (the next 32-row MFMA block) share the
-// swizzle and their addresses differ by a constant.
-template <int CA>
-__device__ __forceinline__ int swz_a(int r) {
-  if constexpr (CA == 8)
-    return (r & 7) ^ ((r >> 3) & 1);
-  else
-    return ((r >> 1) ^ (r >> 3)) & 3;
+// Swizzles.  The hardware serves a 16-byte-per-lane LDS read 8 lanes (128 B) or 16 lanes
+// (256 B) at a time, so the rows touched by any 8 (and any 16) consecutive lanes must land on
+// distinct bank groups.
+//  * k-major, 128-byte rows (BK = 64): 32 lanes read 32 consecutive rows at one logical
+//    chunk; swz = (r mod 8) xor bit 3 of r gives 8 rows 8 distinct chunk positions and 16
+//    rows 16 distinct (row parity, position) pairs.
+//  * k-major, 64-byte rows (BK = 32): two rows share a bank line; swz = (bits 1-2 of r) xor
+//    (bits 3-4) gives distinct (r mod 2, position) over 8 rows and distinct (r mod 4,
+//    position) over 16.
+//    Both depend on r mod 32 only, so rows 32 apart (the next 32-row MFMA block) share the
+//    swizzle and their addresses differ by a constant.
+//  * x-major: a transposing read covers 4 consecutive rows x 2 (16 lanes) or x 4 (32 lanes)
+//    consecutive chunks; the XOR values 0, 10, 4, 14 for r % 4 = 0..3 (masked to the row's
+//    chunk count) spread both footprints over distinct banks.
+template <class O>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (O::KM) {
+    if constexpr (O::CH == 8)
+      return (r & 7) ^ ((r >> 3) & 1);
+    else
+      return ((r >> 1) ^ (r >> 3)) & 3;
+  } else {
+    return ((0xE4A0 >> (4 * (r & 3))) & 0xF) & (O::CH - 1);
+  }
 }
 
-// B panel: BK rows (k) of BN halves; chunk c of row k sits at c ^ swz_b(k).  A transposing
-// read covers 4 consecutive rows x 2 (16 lanes) or x 4 (32 lanes) consecutive chunks; the
-// XOR values 0, 10, 4, 14 for k % 4 = 0..3 spread both footprints over distinct banks.
-template <int CB>
-__device__ __forceinline__ int swz_b(int k) {
-  return ((0xE4A0 >> (4 * (k & 3))) & 0xF) & (CB - 1);
-}
-
-template <class T>
-__device__ __forceinline__ int lds_a(int r, int c) {
-  return r * (T::CA * 16) + ((c ^ swz_a<T::CA>(r)) << 4);
-}
-template <class T>
-__device__ __forceinline__ int lds_b(int k, int n) {
-  return k * (T::CB * 16) + ((((n >> 3) ^ swz_b<T::CB>(k))) << 4) + ((n & 7) << 1);
+// LDS byte offset of logical chunk c of row r of a panel.
+template <class O>
+__device__ __forceinline__ int lds_chunk(int r, int c) {
+  return r * O::ROW_BYTES + ((c ^ swz<O>(r)) << 4);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -161,27 +193,55 @@ struct Frag {
   half8 b[T::TN];
 };
 
-// Per-lane LDS byte offsets of a wave's operand reads inside one stage.  A: one per k step
-// (block tm adds 32 rows, which keep the swizzle, so that is an immediate).  B: one per 32-column block (k step kk and the second
-// 4-deep read add whole rows, which keep row % 4 and hence the swizzle; also immediates).
+// Per-lane LDS byte offsets of a wave's operand reads inside one stage.  k-major: one per k
+// step (block t adds 32 rows, which keep the swizzle, so that is an immediate).  x-major: one
+// per 32-wide block (k step kk and the second 4-deep read add whole rows, which keep
+// row % 4 and hence the swizzle; also immediates).
 template <class T>
 struct LaneOffsets {
-  int a[T::BK / 16];
-  int b[T::TN];
+  int a[T::OA::NOFF];
+  int b[T::OB::NOFF];
 };
+
+template <class O>
+__device__ __forceinline__ void operand_offsets(int (&o)[O::NOFF], int wx, int lane, int base) {
+  if constexpr (O::KM) {
+#pragma unroll
+    for (int kk = 0; kk < O::BK / 16; ++kk)
+      o[kk] = base + lds_chunk<O>(wx * O::WX + (lane & 31), kk * 2 + (lane >> 5));
+  } else {
+    // Lane 4e + j of a 16-lane group g addresses row (g/2)*8 + e and the 4 halves at
+    // x = (g%2)*16 + 4j of its block: the group's 4 x 16 block then transposes into lane
+    // i <- column i, i.e. lane l gets x = l % 32 and k = 8(l/32) + 0..3.
+    const int g = lane >> 4, i = lane & 15;
+#pragma unroll
+    for (int t = 0; t < O::T; ++t) {
+      const int x = wx * O::WX + t * 32 + (g & 1) * 16 + (i & 3) * 4;
+      o[t] = base + lds_chunk<O>((g >> 1) * 8 + (i >> 2), x >> 3) + ((x & 7) << 1);
+    }
+  }
+}
 
 template <class T>
 __device__ __forceinline__ LaneOffsets<T> lane_offsets(int wm, int wn, int lane) {
   LaneOffsets<T> o;
-#pragma unroll
-  for (int kk = 0; kk < T::BK / 16; ++kk)
-    o.a[kk] = lds_a<T>(wm * T::WTM + (lane & 31), kk * 2 + (lane >> 5));
-  const int g = lane >> 4, i = lane & 15;
-#pragma unroll
-  for (int tn = 0; tn < T::TN; ++tn)
-    o.b[tn] = T::A_BYTES +
-              lds_b<T>((g >> 1) * 8 + (i >> 2), wn * T::WTN + tn * 32 + (g & 1) * 16 + (i & 3) * 4);
+  operand_offsets<typename T::OA>(o.a, wm, lane, 0);
+  operand_offsets<typename T::OB>(o.b, wn, lane, T::A_BYTES);
   return o;
+}
+
+// Operand block t of k step kk from the stage at `st`.
+template <class O>
+__device__ __forceinline__ half8 read_operand(const char GK_LDS* st, const int (&o)[O::NOFF],
+                                              int t, int kk) {
+  if constexpr (O::KM) {
+    return *(const half8 GK_LDS*)(st + o[kk] + t * 32 * O::ROW_BYTES);
+  } else {
+    const char GK_LDS* p = st + o[t] + kk * 16 * O::ROW_BYTES;
+    short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((short4v GK_LDS*)p);
+    short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((short4v GK_LDS*)(p + 4 * O::ROW_BYTES));
+    return __builtin_bit_cast(half8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  }
 }
 
 // Reads the operands of k step kk from the stage at `st`.
@@ -189,15 +249,9 @@ template <class T>
 __device__ __forceinline__ void read_frags(Frag<T>& f, const char GK_LDS* st,
                                            const LaneOffsets<T>& o, int kk) {
 #pragma unroll
-  for (int tm = 0; tm < T::TM; ++tm)
-    f.a[tm] = *(const half8 GK_LDS*)(st + o.a[kk] + tm * 32 * (T::CA * 16));
+  for (int tm = 0; tm < T::TM; ++tm) f.a[tm] = read_operand<typename T::OA>(st, o.a, tm, kk);
 #pragma unroll
-  for (int tn = 0; tn < T::TN; ++tn) {
-    const char GK_LDS* pb = st + o.b[tn] + kk * 16 * (T::CB * 16);
-    short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((short4v GK_LDS*)pb);
-    short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((short4v GK_LDS*)(pb + 4 * T::CB * 16));
-    f.b[tn] = __builtin_bit_cast(half8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-  }
+  for (int tn = 0; tn < T::TN; ++tn) f.b[tn] = read_operand<typename T::OB>(st, o.b, tn, kk);
 }
 
 template <class T>
@@ -223,10 +277,11 @@ __device__ __forceinline__ void mma_panel(const char GK_LDS* st, float16v (&acc)
 
 // ---------------------------------------------------------------------------------------
 // Epilogue: narrow once (fp32 -> fp16, round to nearest even) and store the wave's block.
-// Stores go through a buffer resource that ends at C's last element, so rows past M are
-// dropped by the hardware; columns past N (which would land in the ldc padding) are masked.
-// Per lane, one VGPR holds the byte offset of its first element; row steps are scalar
-// offsets and 32-column steps immediates.
+// Only C[i][j] with i < M and j < N is written: columns past N are masked per 32-column block
+// and, in the last tile row, rows past M per element.  (The buffer resource's range check is
+// not relied on: its extent is rounded up to a whole dword, so a store one element past C's
+// last element would still land.)  Per lane, one VGPR holds the byte offset of its first
+// element; row steps are scalar offsets and 32-column steps immediates.
 // ---------------------------------------------------------------------------------------
 template <class T>
 __device__ __forceinline__ void store_tile(const Args& p, const float16v (&acc)[T::TM][T::TN],
@@ -235,25 +290,34 @@ __device__ __forceinline__ void store_tile(const Args& p, const float16v (&acc)[
   const int64_t extC = (int64_t)(p.M - 1) * p.ldc + p.N;
   const __amdgpu_buffer_rsrc_t rc = make_rsrc(p.C + c0, 2 * (extC - c0));
   const int col = wn * T::WTN + (lane & 31);
-  const uint32_t vbase =
-      2u * ((uint32_t)(wm * T::WTM + (lane >> 5) * 4) * (uint32_t)p.ldc + (uint32_t)col);
+  const int row = wm * T::WTM + (lane >> 5) * 4;
+  const uint32_t vbase = 2u * ((uint32_t)row * (uint32_t)p.ldc + (uint32_t)col);
   const uint32_t ldc2 = 2u * (uint32_t)p.ldc;
   const int ncols = p.N - n0;   // columns of this tile that exist
+  const int nrows = p.M - m0;   // rows of this tile that exist
+  auto block = [&](auto all_rows) __attribute__((always_inline)) {
 #pragma unroll
-  for (int tn = 0; tn < T::TN; ++tn) {
-    if (col + tn * 32 < ncols) {
+    for (int tn = 0; tn < T::TN; ++tn) {
+      if (col + tn * 32 < ncols) {
 #pragma unroll
-      for (int tm = 0; tm < T::TM; ++tm) {
+        for (int tm = 0; tm < T::TM; ++tm) {
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const uint32_t rowstep = (uint32_t)(tm * 32 + (v >> 2) * 8 + (v & 3)) * ldc2;
-          const _Float16 h = (_Float16)acc[tm][tn][v];
-          __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, h), rc,
-                                                vbase + tn * 64, rowstep, 0);
+          for (int v = 0; v < 16; ++v) {
+            const int r = tm * 32 + (v >> 2) * 8 + (v & 3);
+            if (decltype(all_rows)::value || row + r < nrows) {
+              const _Float16 h = (_Float16)acc[tm][tn][v];
+              __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, h), rc,
+                                                    vbase + tn * 64, (uint32_t)r * ldc2, 0);
+            }
+          }
         }
       }
     }
-  }
+  };
+  if (nrows >= T::BM)
+    block(std::true_type{});
+  else
+    block(std::false_type{});
 }
 
 // Wait for this wave's LDS accesses, then meet the other waves.  Written as one asm block so
@@ -293,17 +357,114 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 
 // ---------------------------------------------------------------------------------------
-// DMA path (any shape, any 2-byte alignment, any leading dimension).
+// Operand loading for the DMA path.
+//
+// Load slot q = (i*4 + w)*64 + lane of a panel (thread q mod 256 owns it) holds the chunk at
+// position q % CH of LDS row q / CH, i.e. logical chunk (q % CH) ^ swz(row).  Relative to the
+// panel's corner in global memory that chunk starts 2 (row * ld + 8 chunk) bytes in, for
+// either storage order (an LDS row is an x row of a k-major operand, a k row of an x-major
+// one).
+// ---------------------------------------------------------------------------------------
+template <class O>
+__device__ __forceinline__ void slot_offsets(uint32_t (&off)[O::LD], int w, int lane,
+                                             int64_t ld) {
+#pragma unroll
+  for (int i = 0; i < O::LD; ++i) {
+    const int q = (i * 4 + w) * 64 + lane;
+    const int r = q / O::CH, c = (q % O::CH) ^ swz<O>(r);
+    off[i] = 2u * ((uint32_t)r * (uint32_t)ld + (uint32_t)(c * 8));
+  }
+}
+
+// Full panel at (x0, k0), k0 >= 0: 16-byte DMA into the operand's part of a stage.  A panel
+// that is not live gets an empty resource: its loads touch no memory and deposit zeros.
+template <class O>
+__device__ __forceinline__ void dma_panel(const uint16_t* ptr, int64_t ld, int64_t ext, int x0,
+                                          int64_t k0, bool live, const uint32_t (&off)[O::LD],
+                                          char GK_LDS* dst, int w) {
+  const int64_t e0 = elem_off<O::KM>(x0, k0, ld);
+  const __amdgpu_buffer_rsrc_t r = make_rsrc(ptr + (live ? e0 : 0), live ? 2 * (ext - e0) : 0);
+#pragma unroll
+  for (int i = 0; i < O::LD; ++i)
+    buffer_load_lds16(r, (void GK_LDS*)(dst + (i * 4 + w) * 1024), off[i]);
+}
+
+// Head panel at (x0, kofs), kofs < 0: the same slots, through registers, with k < 0 read as
+// zero and never addressed (nothing before the matrix's first element is touched).  k-major:
+// element by element, since a chunk may straddle k = 0; x-major: whole chunks of the rows
+// with k >= 0.
+template <class O>
+__device__ __forceinline__ void head_load(u32x4 (&v)[O::LD], const uint16_t* ptr, int64_t ld,
+                                          int64_t ext, int x0, int kofs, int w, int lane) {
+  const int64_t e0 = elem_off<O::KM>(x0, 0, ld);
+  const __amdgpu_buffer_rsrc_t r = make_rsrc(ptr + e0, 2 * (ext - e0));
+#pragma unroll
+  for (int i = 0; i < O::LD; ++i) {
+    const int q = (i * 4 + w) * 64 + lane;
+    const int row = q / O::CH, c = (q % O::CH) ^ swz<O>(row);
+    if constexpr (O::KM) {
+      uint16_t h[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int k = kofs + c * 8 + e;
+        h[e] = k >= 0 ? __builtin_amdgcn_raw_buffer_load_b16(
+                            r, 2u * ((uint32_t)row * (uint32_t)ld + (uint32_t)k), 0, 0)
+                      : (uint16_t)0;
+      }
+#pragma unroll
+      for (int d = 0; d < 4; ++d) v[i][d] = (uint32_t)h[2 * d] | ((uint32_t)h[2 * d + 1] << 16);
+    } else {
+      const int k = kofs + row;
+      v[i] = k >= 0 ? __builtin_amdgcn_raw_buffer_load_b128(
+                          r, 2u * ((uint32_t)k * (uint32_t)ld + (uint32_t)(c * 8)), 0, 0)
+                    : u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+}
+
+template <class O>
+__device__ __forceinline__ void head_store(const u32x4 (&v)[O::LD], char GK_LDS* dst, int w,
+                                           int lane) {
+#pragma unroll
+  for (int i = 0; i < O::LD; ++i) *(u32x4 GK_LDS*)(dst + ((i * 4 + w) * 64 + lane) * 16) = v[i];
+}
+
+// The operand's last element (X-1, K-1) in the last panel.  A 16-byte load that starts 2
+// bytes into a dword is range-checked dword by dword from its own start, so when the matrix
+// ends on a 4-byte boundary the dword holding its last element reaches 2 bytes past the end
+// and reads as zero.  The thread whose load slot holds that element (local k = BK-1 of the
+// last panel, in the tile that contains x = X-1) rewrites it from an exact 2-byte load once
+// the panel has landed.  Returns the element's LDS byte offset within the operand's part of
+// a stage (and its value), or -1 for every other thread.
+template <class O>
+__device__ __forceinline__ int last_element_slot(int x0, int X, int K, const uint16_t* ptr,
+                                                 int64_t ext, uint16_t& value) {
+  const int xl = X - 1 - x0;
+  if (K <= 0 || xl >= O::BX) return -1;
+  int q, byte;
+  if constexpr (O::KM) {
+    q = xl * O::CH + ((O::CH - 1) ^ swz<O>(xl));
+    byte = 7 * 2;
+  } else {
+    q = (O::BK - 1) * O::CH + ((xl >> 3) ^ swz<O>(O::BK - 1));
+    byte = (xl & 7) * 2;
+  }
+  if ((q & (kThreads - 1)) != (int)threadIdx.x) return -1;
+  value = __builtin_amdgcn_raw_buffer_load_b16(make_rsrc(ptr + ext - 1, 2), 0u, 0, 0);
+  return q * 16 + byte;
+}
+
+// ---------------------------------------------------------------------------------------
+// DMA path (any shape, any 2-byte alignment, any leading dimension, either storage order of
+// each operand).
 //
 // Panels are BK deep.  When BK does not divide K, panel 0 is a "head" that holds the first
 // K mod BK values of k at its end and zeros in front: the run is then the same, bit for bit,
 // as a run on operands zero-padded in front of k to a multiple of BK, and every later panel
-// is a full one.  Full panels are loaded with 16-byte buffer->LDS DMA (A: rows of 16-byte
-// chunks, B: 16-byte chunks of rows); the buffer resources end at the matrices' last
-// elements, so rows past M read as zeros and nothing past the matrices is read.  Columns
-// past N read whatever lies there and only feed results that are never stored.  The head is
-// loaded through registers, A element by element (so nothing before A's first element is
-// ever addressed), and written to LDS in the same layout.
+// is a full one.  Full panels are loaded with 16-byte buffer->LDS DMA; the buffer resources
+// end at the matrices' last elements, so nothing past a matrix is read (it reads as zero).
+// Rows and columns past M or N only feed results that are never stored.  The head is loaded
+// through registers and written to LDS in the same layout.
 //
 // Pipeline (per wave), NS LDS stages, panel s in stage s mod NS: the operands of k step kk+1
 // are read from LDS while the MFMAs of step kk run.  The one barrier per panel sits in the
@@ -314,12 +475,14 @@ __device__ __forceinline__ void wait_vmcnt() {
 // resources: they load zeros, touch no memory and add exactly +0, which keeps the loop free
 // of branches.
 // ---------------------------------------------------------------------------------------
-template <int BM, int BN, int BK, int NS>
+template <int BM, int BN, int BK, int NS, bool AKM, bool BKM>
 __global__ void __launch_bounds__(kThreads) gemm_dma(Args p) {
-  using T = Tile<BM, BN, BK>;
+  using T = Tile<BM, BN, BK, AKM, BKM>;
+  using OA = typename T::OA;
+  using OB = typename T::OB;
   constexpr int KS = BK / 16;              // k steps per panel
   constexpr int NM = T::TM * T::TN;        // MFMAs per k step
-  constexpr int ND = T::TM + 2 * T::TN;    // LDS reads per k step
+  constexpr int ND = OA::READS + OB::READS;  // LDS reads per k step
   constexpr int NV = T::A_LD + T::B_LD;    // buffer->LDS loads per panel
   static_assert(KS % 2 == 0 && NS >= 2 && NS <= 5, "pipeline shape");
   static_assert(NS * T::STAGE <= 160 * 1024, "LDS");
@@ -338,117 +501,39 @@ __global__ void __launch_bounds__(kThreads) gemm_dma(Args p) {
                pid, pid_m, pid_n);
   const int m0 = pid_m * BM, n0 = pid_n * BN;
 
-  // This thread's load slots: slot q = (i*4 + w)*64 + lane of a stage holds logical chunk
-  // (row, chunk) of A (or B) as given by the swizzles.  Byte offsets relative to the panel's
-  // corner.
   uint32_t offA[T::A_LD], offB[T::B_LD];
-#pragma unroll
-  for (int i = 0; i < T::A_LD; ++i) {
-    const int q = (i * 4 + w) * 64 + lane;
-    const int r = q / T::CA, c = (q % T::CA) ^ swz_a<T::CA>(r);
-    offA[i] = 2u * ((uint32_t)r * (uint32_t)p.lda + (uint32_t)(c * 8));
-  }
-#pragma unroll
-  for (int i = 0; i < T::B_LD; ++i) {
-    const int q = (i * 4 + w) * 64 + lane;
-    const int k = q / T::CB, c = (q % T::CB) ^ swz_b<T::CB>(k);
-    offB[i] = 2u * ((uint32_t)k * (uint32_t)p.ldb + (uint32_t)(c * 8));
-  }
+  slot_offsets<OA>(offA, w, lane, p.lda);
+  slot_offsets<OB>(offB, w, lane, p.ldb);
 
-  // Extents (elements from each matrix's first element to one past its last).
-  const int64_t extA = (int64_t)(p.M - 1) * p.lda + p.K;
-  const int64_t extB = (int64_t)(p.K - 1) * p.ldb + p.N;
+  const int64_t extA = extent<AKM>(p.M, p.K, p.lda);
+  const int64_t extB = extent<BKM>(p.N, p.K, p.ldb);
   const int rk = p.K % BK;                       // depth of the head panel (0: none)
   const int np = p.K / BK + (rk ? 1 : 0);        // panels
   const int kofs = rk ? rk - BK : 0;             // panel s covers k in [kofs + s BK, + BK)
 
-  // The last panel's copies of A's last element A[M-1][K-1] and B's last element
-  // B[K-1][N-1].  A 16-byte load that starts 2 bytes into a dword is range-checked dword by
-  // dword from its own start, so when a matrix ends on a 4-byte boundary the dword holding its
-  // last element reaches 2 bytes past the end and reads as zero.  The thread whose load slot
-  // holds that element (local k = BK-1 of the last panel, for tiles that contain row M-1 or
-  // column N-1) rewrites it from an exact 2-byte load once the panel has landed.
-  int patch_a = -1, patch_b = -1;    // LDS byte offsets within a stage, or -1
   uint16_t last_a = 0, last_b = 0;
-  {
-    const int t = threadIdx.x;
-    const int rl = p.M - 1 - m0;
-    if (p.K > 0 && rl < BM) {
-      const int q = rl * T::CA + ((T::CA - 1) ^ swz_a<T::CA>(rl));
-      if ((q & (kThreads - 1)) == t) {
-        patch_a = q * 16 + 7 * 2;
-        last_a = __builtin_amdgcn_raw_buffer_load_b16(
-            make_rsrc(p.A, 2 * extA), 2u * (uint32_t)((int64_t)(p.M - 1) * p.lda + p.K - 1), 0, 0);
-      }
-    }
-    const int cl = p.N - 1 - n0;
-    if (p.K > 0 && cl < BN) {
-      const int q = (BK - 1) * T::CB + ((cl >> 3) ^ swz_b<T::CB>(BK - 1));
-      if ((q & (kThreads - 1)) == t) {
-        patch_b = T::A_BYTES + q * 16 + (cl & 7) * 2;
-        last_b = __builtin_amdgcn_raw_buffer_load_b16(
-            make_rsrc(p.B, 2 * extB), 2u * (uint32_t)((int64_t)(p.K - 1) * p.ldb + p.N - 1), 0, 0);
-      }
-    }
-  }
+  const int patch_a = last_element_slot<OA>(m0, p.M, p.K, p.A, extA, last_a);
+  const int patch_b = last_element_slot<OB>(n0, p.N, p.K, p.B, extB, last_b);
   auto patch = [&](char GK_LDS* base) __attribute__((always_inline)) {
     if (patch_a >= 0) *(uint16_t GK_LDS*)(base + patch_a) = last_a;
-    if (patch_b >= 0) *(uint16_t GK_LDS*)(base + patch_b) = last_b;
+    if (patch_b >= 0) *(uint16_t GK_LDS*)(base + T::A_BYTES + patch_b) = last_b;
   };
 
-  // Full panel s (k0 = kofs + s BK >= 0): DMA into `base`.  Panels past the end get an empty
-  // resource: their loads touch no memory and deposit zeros.
+  // Full panel s (k0 = kofs + s BK >= 0) into `base`; panels s >= np load zeros.
   auto issue = [&](int s, char GK_LDS* base) __attribute__((always_inline)) {
     const bool live = s < np;
     const int64_t k0 = (int64_t)kofs + (int64_t)s * BK;
-    const int64_t a0 = (int64_t)m0 * p.lda + k0;
-    const int64_t b0 = k0 * p.ldb + n0;
-    const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.A + (live ? a0 : 0), live ? 2 * (extA - a0) : 0);
-    const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.B + (live ? b0 : 0), live ? 2 * (extB - b0) : 0);
-#pragma unroll
-    for (int i = 0; i < T::A_LD; ++i)
-      buffer_load_lds16(ra, (void GK_LDS*)(base + (i * 4 + w) * 1024), offA[i]);
-#pragma unroll
-    for (int i = 0; i < T::B_LD; ++i)
-      buffer_load_lds16(rb, (void GK_LDS*)(base + T::A_BYTES + (i * 4 + w) * 1024), offB[i]);
+    dma_panel<OA>(p.A, p.lda, extA, m0, k0, live, offA, base, w);
+    dma_panel<OB>(p.B, p.ldb, extB, n0, k0, live, offB, base + T::A_BYTES, w);
   };
 
-  // Head panel (k0 = kofs < 0): the same slots, through registers; k < 0 is zero.
+  // Head panel (k0 = kofs < 0).
   auto head = [&](char GK_LDS* base) __attribute__((always_inline)) {
-    const int64_t a0 = (int64_t)m0 * p.lda;
-    const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.A + a0, 2 * (extA - a0));
-    const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.B + n0, 2 * (extB - n0));
     u32x4 va[T::A_LD], vb[T::B_LD];
-#pragma unroll
-    for (int i = 0; i < T::A_LD; ++i) {
-      const int q = (i * 4 + w) * 64 + lane;
-      const int r = q / T::CA, c = (q % T::CA) ^ swz_a<T::CA>(r);
-      uint16_t h[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int k = kofs + c * 8 + e;
-        h[e] = k >= 0 ? __builtin_amdgcn_raw_buffer_load_b16(
-                            ra, 2u * ((uint32_t)r * (uint32_t)p.lda + (uint32_t)k), 0, 0)
-                      : (uint16_t)0;
-      }
-#pragma unroll
-      for (int d = 0; d < 4; ++d) va[i][d] = (uint32_t)h[2 * d] | ((uint32_t)h[2 * d + 1] << 16);
-    }
-#pragma unroll
-    for (int i = 0; i < T::B_LD; ++i) {
-      const int q = (i * 4 + w) * 64 + lane;
-      const int k = q / T::CB, c = (q % T::CB) ^ swz_b<T::CB>(k);
-      const int kr = kofs + k;
-      vb[i] = kr >= 0 ? __builtin_amdgcn_raw_buffer_load_b128(
-                            rb, 2u * ((uint32_t)kr * (uint32_t)p.ldb + (uint32_t)(c * 8)), 0, 0)
-                      : u32x4{0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int i = 0; i < T::A_LD; ++i)
-      *(u32x4 GK_LDS*)(base + ((i * 4 + w) * 64 + lane) * 16) = va[i];
-#pragma unroll
-    for (int i = 0; i < T::B_LD; ++i)
-      *(u32x4 GK_LDS*)(base + T::A_BYTES + ((i * 4 + w) * 64 + lane) * 16) = vb[i];
+    head_load<OA>(va, p.A, p.lda, extA, m0, kofs, w, lane);
+    head_load<OB>(vb, p.B, p.ldb, extB, n0, kofs, w, lane);
+    head_store<OA>(va, base, w, lane);
+    head_store<OB>(vb, base + T::A_BYTES, w, lane);
   };
 
   float16v acc[T::TM][T::TN];
@@ -522,10 +607,11 @@ __global__ void __launch_bounds__(kThreads) gemm_dma(Args p) {
 }
 
 // ---------------------------------------------------------------------------------------
-// Generic path: any leading dimension, any 2-byte alignment, any K.  Panels are fetched with
-// raw buffer loads whose resource ends at the matrix's last element, so reads past it return
-// zero and never fault; A's elements at k >= K inside a row are zeroed explicitly.  kOdd:
-// some row starts are only 2-byte aligned, so each 16-byte chunk is assembled from a
+// Generic path: any leading dimension, any 2-byte alignment, any K, either storage order of
+// each operand.  Panels are fetched with raw buffer loads whose resource ends at the
+// matrix's last element, so reads past it return zero and never fault; chunks of a k-major
+// operand that reach k >= K are zeroed explicitly (x-major rows k >= K lie past the end).
+// kOdd: some row starts are only 2-byte aligned, so each 16-byte chunk is assembled from a
 // 4-byte-aligned dwordx4 plus one more dword and a byte funnel shift.
 // ---------------------------------------------------------------------------------------
 template <bool kOdd>
@@ -557,9 +643,40 @@ __device__ __forceinline__ u32x4 mask_k(u32x4 v, int first, int K) {
   return v;
 }
 
-template <int BM, int BN, bool kOdd>
+// Slot q = i*256 + t of a panel holds logical chunk q % CH of LDS row q / CH.
+template <class O, bool kOdd>
+__device__ __forceinline__ void generic_fetch(u32x4 (&v)[O::LD], const uint16_t* ptr,
+                                              int64_t ld, int64_t ext, int x0, int k0, int K,
+                                              int t) {
+  const int64_t e0 = elem_off<O::KM>(x0, k0, ld);
+  const __amdgpu_buffer_rsrc_t r = make_rsrc(ptr + e0, 2 * (ext - e0));
+  const bool tail = k0 + O::BK > K;
+#pragma unroll
+  for (int i = 0; i < O::LD; ++i) {
+    const int q = i * kThreads + t;
+    const int row = q / O::CH, c = q % O::CH;
+    v[i] = load_chunk<kOdd>(r, 2u * ((uint32_t)row * (uint32_t)ld + (uint32_t)(c * 8)));
+    if constexpr (O::KM) {
+      if (tail) v[i] = mask_k(v[i], k0 + c * 8, K);
+    }
+  }
+}
+
+template <class O>
+__device__ __forceinline__ void generic_deposit(const u32x4 (&v)[O::LD], char GK_LDS* dst,
+                                                int t) {
+#pragma unroll
+  for (int i = 0; i < O::LD; ++i) {
+    const int q = i * kThreads + t;
+    *(u32x4 GK_LDS*)(dst + lds_chunk<O>(q / O::CH, q % O::CH)) = v[i];
+  }
+}
+
+template <int BM, int BN, bool kOdd, bool AKM, bool BKM>
 __global__ void __launch_bounds__(kThreads) gemm_generic(Args p) {
-  using T = Tile<BM, BN>;
+  using T = Tile<BM, BN, kBK, AKM, BKM>;
+  using OA = typename T::OA;
+  using OB = typename T::OB;
   __shared__ __attribute__((aligned(16))) char smem[2 * T::STAGE];
 
   const int t = threadIdx.x;
@@ -572,50 +689,18 @@ __global__ void __launch_bounds__(kThreads) gemm_generic(Args p) {
                pid, pid_m, pid_n);
   const int m0 = pid_m * BM, n0 = pid_n * BN;
   const int nk = (p.K + T::BK - 1) / T::BK;
-
-  // Extents in elements, from each matrix's first element to one past its last.
-  const int64_t extA = (int64_t)(p.M - 1) * p.lda + p.K;
-  const int64_t extB = (int64_t)(p.K - 1) * p.ldb + p.N;
+  const int64_t extA = extent<AKM>(p.M, p.K, p.lda);
+  const int64_t extB = extent<BKM>(p.N, p.K, p.ldb);
 
   u32x4 ra[T::A_LD], rb[T::B_LD];
-
-  auto fetch = [&](int s) {
-    const int k0 = s * T::BK;
-    const int64_t baseA = (int64_t)m0 * p.lda + k0;
-    const int64_t baseB = (int64_t)k0 * p.ldb + n0;
-    __amdgpu_buffer_rsrc_t rsA = make_rsrc(p.A + baseA, 2 * (extA - baseA));
-    __amdgpu_buffer_rsrc_t rsB = make_rsrc(p.B + baseB, 2 * (extB - baseB));
-    const bool tail = k0 + T::BK > p.K;
-#pragma unroll
-    for (int i = 0; i < T::A_LD; ++i) {
-      const int q = i * kThreads + t;
-      const int r = q / T::CA, c = q % T::CA;
-      const uint32_t off = 2u * ((uint32_t)r * (uint32_t)p.lda + (uint32_t)(c * 8));
-      ra[i] = load_chunk<kOdd>(rsA, off);
-      if (tail) ra[i] = mask_k(ra[i], k0 + c * 8, p.K);
-    }
-#pragma unroll
-    for (int i = 0; i < T::B_LD; ++i) {
-      const int q = i * kThreads + t;
-      const int k = q / T::CB, c = q % T::CB;
-      const uint32_t off = 2u * ((uint32_t)k * (uint32_t)p.ldb + (uint32_t)(c * 8));
-      rb[i] = load_chunk<kOdd>(rsB, off);
-    }
+  auto fetch = [&](int s) __attribute__((always_inline)) {
+    generic_fetch<OA, kOdd>(ra, p.A, p.lda, extA, m0, s * T::BK, p.K, t);
+    generic_fetch<OB, kOdd>(rb, p.B, p.ldb, extB, n0, s * T::BK, p.K, t);
   };
-  auto deposit = [&](int stage) {
+  auto deposit = [&](int stage) __attribute__((always_inline)) {
     char GK_LDS* base = (char GK_LDS*)smem + stage * T::STAGE;
-#pragma unroll
-    for (int i = 0; i < T::A_LD; ++i) {
-      const int q = i * kThreads + t;
-      const int r = q / T::CA, c = q % T::CA;
-      *(u32x4 GK_LDS*)(base + lds_a<T>(r, c)) = ra[i];
-    }
-#pragma unroll
-    for (int i = 0; i < T::B_LD; ++i) {
-      const int q = i * kThreads + t;
-      const int k = q / T::CB, c = q % T::CB;
-      *(u32x4 GK_LDS*)(base + T::A_BYTES + lds_b<T>(k, c * 8)) = rb[i];
-    }
+    generic_deposit<OA>(ra, base, t);
+    generic_deposit<OB>(rb, base + T::A_BYTES, t);
   };
 
   const LaneOffsets<T> lo = lane_offsets<T>(wm, wn, lane);

@@ -17,10 +17,14 @@
  * be permuted so that consecutive program ids share one XCD's L2 (gemm_f16f32_tile_map
  * documents the permutation).
  *
- * Layout: all matrices are row-major with unit stride along a row and a leading dimension
- * (elements between the starts of consecutive rows): A[i][k] is at A + i*lda + k, B[k][j] at
- * B + k*ldb + j, C[i][j] at C + i*ldc + j (the stride convention of the notebook's cell
- * In[8]).  Values are IEEE binary16 bit patterns passed as uint16_t.
+ * Layout: gemm_f16f32, gemm_f16f32_ex and gemm_f16f32_plan take row-major matrices with unit
+ * stride along a row and a leading dimension (elements between the starts of consecutive
+ * rows): A[i][k] is at A + i*lda + k, B[k][j] at B + k*ldb + j, C[i][j] at C + i*ldc + j.
+ * gemm_f16f32_strided takes the notebook's general form (cell In[8] derives every pointer
+ * from stride_am, stride_ak, stride_bk, stride_bn): A[i][k] at A + i*stride_am +
+ * k*stride_ak, and likewise for B and C, with one unit stride per matrix (row- or
+ * column-major storage, any leading dimension).  Values are IEEE binary16 bit patterns passed
+ * as uint16_t.
  *
  * Ownership and execution: A, B, C are device pointers owned by the caller.  The library
  * allocates nothing and keeps no state between calls, so calls from several host threads are
@@ -46,10 +50,15 @@ enum {
     GEMM_F16F32_OK = 0,
     GEMM_F16F32_ERR_DIM = -1,       /* M, N or K negative, or >= 2^31 */
     GEMM_F16F32_ERR_NULL = -2,      /* a NULL pointer for a non-empty operand */
-    GEMM_F16F32_ERR_LD = -3,        /* lda < max(K,1), ldb < max(N,1) or ldc < max(N,1) */
+    GEMM_F16F32_ERR_LD = -3,        /* lda < max(K,1), ldb < max(N,1) or ldc < max(N,1);
+                                       strided: a matrix with no unit stride, or a leading
+                                       stride below its row (column) length */
     GEMM_F16F32_ERR_OVERLAP = -4,   /* C's footprint overlaps A's or B's */
     GEMM_F16F32_ERR_OPTS = -5,      /* an option outside its range, or an odd pointer address */
-    GEMM_F16F32_ERR_TOO_LARGE = -6, /* a leading dimension beyond the kernels' 32-bit offsets */
+    GEMM_F16F32_ERR_TOO_LARGE = -6, /* a leading dimension beyond the kernels' 32-bit offsets:
+                                       BM * ldc, and for each operand (rows of one stored
+                                       panel) * ld must stay below 2^31, where a panel has BM
+                                       (BN) rows when k is the unit-stride axis, else 64 */
     GEMM_F16F32_ERR_HIP = -7        /* the HIP runtime rejected the launch */
 };
 
@@ -104,6 +113,13 @@ typedef struct gemm_f16f32_plan_info {
     int32_t launches;      /* kernel launches the call makes (1 + edge strips; 0 if empty) */
     int32_t main_m;        /* rows of C covered by the launch described above */
     int32_t main_n;        /* columns of C covered by the launch described above */
+    int32_t a_kmajor;      /* 1: the launch's first operand has consecutive k adjacent in
+                              memory (A row-major); 0: consecutive rows adjacent */
+    int32_t b_kmajor;      /* 1: the launch's second operand has consecutive k adjacent (B
+                              column-major); 0: consecutive columns adjacent (B row-major) */
+    int32_t swapped;       /* 1: C is column-major and the launch computes C^T = B^T A^T; its
+                              first operand is then B^T, and bm, num_pid_m, main_m run along
+                              N, bn, num_pid_n, main_n along M */
 } gemm_f16f32_plan_info;
 
 /*
@@ -125,6 +141,31 @@ int gemm_f16f32_ex(int64_t M, int64_t N, int64_t K, const uint16_t *A, const uin
 int gemm_f16f32_plan(int64_t M, int64_t N, int64_t K, const uint16_t *A, const uint16_t *B,
                      const uint16_t *C, int64_t lda, int64_t ldb, int64_t ldc,
                      const gemm_f16f32_opts *opts, gemm_f16f32_plan_info *info);
+
+/*
+ * C[0:M, 0:N] = fp16( A[0:M, 0:K] . B[0:K, 0:N] ) for matrices given by element strides, the
+ * general form of the notebook's cell In[8]: A[i][k] at A + i*stride_am + k*stride_ak,
+ * B[k][j] at B + k*stride_bk + j*stride_bn, C[i][j] at C + i*stride_cm + j*stride_cn.
+ * Each matrix must be row-major (column stride 1, row stride >= its column count) or
+ * column-major (row stride 1, column stride >= its row count); a stride along an axis of
+ * extent 1 is ignored, and an empty matrix may have any strides.  Anything else returns
+ * GEMM_F16F32_ERR_LD.  All four storage orders of A and B run on the same kernels (an
+ * operand stored with k contiguous is staged as rows of k, the other order as rows of i or
+ * j), and every element gets the same fp32 k-sum as in the row-major call, bit for bit.  A
+ * column-major C is computed as its transpose, C^T = B^T A^T.  Other arguments, ownership,
+ * asynchrony and errors as for gemm_f16f32_ex.
+ */
+int gemm_f16f32_strided(int64_t M, int64_t N, int64_t K, const uint16_t *A, int64_t stride_am,
+                        int64_t stride_ak, const uint16_t *B, int64_t stride_bk,
+                        int64_t stride_bn, uint16_t *C, int64_t stride_cm, int64_t stride_cn,
+                        void *stream, const gemm_f16f32_opts *opts);
+
+/* Host only, no GPU work: what gemm_f16f32_strided with these arguments would launch. */
+int gemm_f16f32_strided_plan(int64_t M, int64_t N, int64_t K, const uint16_t *A,
+                             int64_t stride_am, int64_t stride_ak, const uint16_t *B,
+                             int64_t stride_bk, int64_t stride_bn, const uint16_t *C,
+                             int64_t stride_cm, int64_t stride_cn, const gemm_f16f32_opts *opts,
+                             gemm_f16f32_plan_info *info);
 
 /*
  * Writes, for every hardware workgroup id h in [0, P), P = num_pid_m * num_pid_n, the

@@ -147,3 +147,84 @@ def test_edge_split_plans(M, N, want):
     # a forced tile splits only when asked
     assert plan(M, N, 512, tile=g.TILE_256x256x64)["launches"] == 1
     assert plan(M, N, 512, tile=g.TILE_256x256x64, split_edges=g.SPLIT_ON)["launches"] >= 1
+
+
+# ---- strided entry points ------------------------------------------------------------------
+
+def splan(M, N, K, sa, sb, sc, a=PA, b=PB, c=PC, **opts):
+    return g.gemm_f16f32_strided_plan(M, N, K, a, sa[0], sa[1], b, sb[0], sb[1], c, sc[0],
+                                      sc[1], opts=opts or None)
+
+
+def test_strided_row_major_matches_plain_plan():
+    M, N, K = 4096, 4096, 4096
+    rc, p = splan(M, N, K, (K, 1), (N, 1), (N, 1))
+    assert rc == g.OK
+    assert p == plan(M, N, K)
+    assert (p["a_kmajor"], p["b_kmajor"], p["swapped"]) == (1, 0, 0)
+
+
+@pytest.mark.parametrize("a_col,b_col", [(0, 0), (0, 1), (1, 0), (1, 1)])
+@pytest.mark.parametrize("c_col", [0, 1])
+def test_strided_layouts(a_col, b_col, c_col):
+    """Each storage order maps to the kernels' operand orders; a column-major C swaps roles."""
+    M, N, K = 1000, 600, 300
+    sa = (1, M + 8) if a_col else (K + 8, 1)
+    sb = (1, K + 8) if b_col else (N + 8, 1)
+    sc = (1, M + 8) if c_col else (N + 8, 1)
+    rc, p = splan(M, N, K, sa, sb, sc)
+    assert rc == g.OK
+    if not c_col:
+        assert (p["a_kmajor"], p["b_kmajor"], p["swapped"]) == (1 - a_col, b_col, 0)
+        assert (p["num_pid_m"], p["num_pid_n"]) == (-(-M // p["bm"]), -(-N // p["bn"]))
+    else:
+        # C^T = B^T A^T: first operand B^T is k-major iff B is column-major, A^T iff A is
+        # row-major; the launch's rows run along N
+        assert (p["a_kmajor"], p["b_kmajor"], p["swapped"]) == (b_col, 1 - a_col, 1)
+        assert (p["num_pid_m"], p["num_pid_n"]) == (-(-N // p["bm"]), -(-M // p["bn"]))
+
+
+@pytest.mark.parametrize("sa,sb,sc", [
+    ((300, 2), (600, 1), (600, 1)),      # A: no unit stride
+    ((300, 1), (1, 1), (600, 1)),        # B: row-major needs sbk >= N, column-major sbn >= K
+    ((299, 1), (600, 1), (600, 1)),      # A: row stride below K
+    ((1, 999), (600, 1), (600, 1)),      # A column-major: column stride below M
+    ((300, 1), (600, 1), (600, -1)),     # C: negative stride
+    ((300, 1), (600, 1), (0, 1)),        # C: zero row stride
+])
+def test_strided_errors(sa, sb, sc):
+    assert splan(1000, 600, 300, sa, sb, sc)[0] == g.ERR_LD
+    assert g.gemm_f16f32_strided(1000, 600, 300, PA, sa[0], sa[1], PB, sb[0], sb[1], PC,
+                                 sc[0], sc[1], None) == g.ERR_LD
+
+
+def test_strided_degenerate_axes():
+    # a stride along an axis of extent 1 is never used
+    assert splan(1, 600, 300, (12345, 1), (600, 1), (7, 1))[0] == g.OK
+    assert splan(1000, 1, 300, (300, 1), (1, 999), (1, 55))[0] == g.OK
+    assert splan(1000, 600, 1, (1, 3), (600, 1), (600, 1))[0] == g.OK
+    # empty matrices may have any strides; M == 0 launches nothing
+    rc, p = splan(0, 600, 300, (0, 0), (600, 1), (0, 0))
+    assert rc == g.OK and p["num_programs"] == 0
+    rc, p = splan(8, 8, 0, (0, 0), (0, 0), (8, 1), a=0, b=0)
+    assert rc == g.OK and p["num_programs"] > 0
+    assert g.gemm_f16f32_strided(-1, 8, 8, PA, 8, 1, PB, 8, 1, PC, 8, 1, None) == g.ERR_DIM
+
+
+def test_strided_overlap_uses_the_storage_footprint():
+    # A column-major (K x M in memory): footprint 2((K-1) lda + M) bytes
+    M, N, K = 64, 64, 64
+    fa = 2 * ((K - 1) * M + M)
+    assert splan(M, N, K, (1, M), (N, 1), (N, 1), c=PA + fa)[0] == g.OK
+    assert splan(M, N, K, (1, M), (N, 1), (N, 1), c=PA + fa - 2)[0] == g.ERR_OVERLAP
+
+
+def test_too_large_c_leading_dimension():
+    # 64 rows of C at ldc = 2^25 reach 2^31 elements: beyond the store offsets
+    args = (256, 8, 8, 1 << 40, 2 << 40, 3 << 40, 8, 8, 1 << 25)
+    assert g.gemm_f16f32_plan(*args)[0] == g.ERR_TOO_LARGE
+    args = (256, 8, 8, 1 << 40, 2 << 40, 3 << 40, 8, 8, 1 << 24)
+    assert g.gemm_f16f32_plan(*args)[0] == g.OK
+    # a transposed operand's panel spans 64 k rows: 64 x lda
+    assert splan(8, 8, 8, (1, 1 << 25), (8, 1), (8, 1), a=1 << 40, b=2 << 40,
+                 c=3 << 40)[0] == g.ERR_TOO_LARGE

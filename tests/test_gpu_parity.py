@@ -302,3 +302,29 @@ def test_one_hot_last_k_selects_last_row_of_b():
     _, B = operands(1, N, K, "u(-0.5,0.5)", 9)
     C = from_dev(run(to_dev(A), to_dev(B), M, N, K))
     assert np.array_equal(C, np.broadcast_to(B[K - 1], (M, N)))
+
+
+def test_graph_capture_replays_match_eager():
+    """The library launches on the caller's stream, so a HIP graph captured around calls
+    replays them; every replay (with eager work in between) must match the eager result."""
+    M, N, K = 1000, 1100, 900
+    A, B = operands(M, N, K, "u(-0.5,0.5)", 21)
+    Ad, Bd = to_dev(A), to_dev(B)
+    eager = from_dev(run(Ad, Bd, M, N, K))
+    Cg = torch.zeros((M, N), dtype=torch.int16, device="cuda")
+    graph = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        run(Ad, Bd, M, N, K, C_dev=Cg)          # warm-up on the side stream
+    torch.cuda.current_stream().wait_stream(s)
+    with torch.cuda.graph(graph):
+        run(Ad, Bd, M, N, K, C_dev=Cg)
+    for rep in range(3):
+        Cg.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(from_dev(Cg), eager), rep
+        other = from_dev(run(Ad, Bd, 500, 600, K))   # unrelated eager work in between
+        assert_within_tolerance(other, eager[:500, :600], "eager between replays")
