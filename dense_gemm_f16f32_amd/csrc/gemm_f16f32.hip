@@ -11,21 +11,30 @@ namespace {
 
 constexpr int kVersion = 200;  // 0.2.0
 
-// bk: panel depth of the DMA kernel (the generic kernel always uses 64-deep panels);
-// stages: LDS stages of the DMA kernel.
+// The tile configurations: id, BM x BN x BK, NS LDS stages of the DMA kernel, operands read
+// RD k steps ahead, WM x WN wavefronts, default GROUP_SIZE_M.  (The generic kernel stages
+// 64-deep panels through registers for every tile.)
+#define GEMM_F16F32_TILES(X)                                              \
+  X(GEMM_F16F32_TILE_256x256x64, 256, 256, 64, 2, 1, 2, 2, 8)            \
+  X(GEMM_F16F32_TILE_128x128x64, 128, 128, 64, 2, 3, 2, 2, 4)            \
+  X(GEMM_F16F32_TILE_128x64x64, 128, 64, 64, 2, 1, 2, 2, 4)              \
+  X(GEMM_F16F32_TILE_256x128x64, 256, 128, 64, 2, 3, 2, 2, 8)            \
+  X(GEMM_F16F32_TILE_256x256x32, 256, 256, 32, 4, 1, 2, 2, 8)            \
+  X(GEMM_F16F32_TILE_64x64x32, 64, 64, 32, 5, 1, 2, 2, 4)                \
+  X(GEMM_F16F32_TILE_128x64x32, 128, 64, 32, 5, 1, 2, 2, 4)              \
+  X(GEMM_F16F32_TILE_256x256x64_W8, 256, 256, 64, 2, 1, 2, 4, 8)         \
+  X(GEMM_F16F32_TILE_64x64x64, 64, 64, 64, 4, 3, 2, 2, 4)                \
+  X(GEMM_F16F32_TILE_32x32x64, 32, 32, 64, 4, 3, 1, 1, 4)                \
+  X(GEMM_F16F32_TILE_32x64x64, 32, 64, 64, 4, 3, 1, 2, 4)                \
+  X(GEMM_F16F32_TILE_64x32x64, 64, 32, 64, 4, 3, 2, 1, 4)
+
 struct TileDesc {
-  int id, bm, bn, bk, stages, default_group;
+  int id, bm, bn, bk, stages, read_ahead, wm, wn, default_group;
 };
 
-constexpr TileDesc kTiles[] = {
-    {GEMM_F16F32_TILE_256x256x64, 256, 256, 64, 2, 8},
-    {GEMM_F16F32_TILE_128x128x64, 128, 128, 64, 2, 4},
-    {GEMM_F16F32_TILE_128x64x64, 128, 64, 64, 2, 4},
-    {GEMM_F16F32_TILE_256x128x64, 256, 128, 64, 2, 8},
-    {GEMM_F16F32_TILE_256x256x32, 256, 256, 32, 4, 8},
-    {GEMM_F16F32_TILE_64x64x32, 64, 64, 32, 5, 4},
-    {GEMM_F16F32_TILE_128x64x32, 128, 64, 32, 5, 4},
-};
+#define GEMM_F16F32_TILE_DESC(id, bm, bn, bk, ns, rd, wm, wn, g) {id, bm, bn, bk, ns, rd, wm, wn, g},
+constexpr TileDesc kTiles[] = {GEMM_F16F32_TILES(GEMM_F16F32_TILE_DESC)};
+#undef GEMM_F16F32_TILE_DESC
 
 const TileDesc* find_tile(int id) {
   for (const TileDesc& t : kTiles)
@@ -126,6 +135,7 @@ int plan_launch(const Problem& pr, int64_t M, int64_t N, const TileDesc* t,
   r->bm = t->bm;
   r->bn = t->bn;
   r->bk = dma ? t->bk : gk::kBK;
+  r->threads = 64 * t->wm * t->wn;
   r->group_m = o.group_m ? o.group_m : t->default_group;
   r->xcd_remap = (o.xcd_remap == 2) ? 0 : 1;
   const bool empty = (M == 0 || N == 0);
@@ -214,27 +224,34 @@ int plan_parts(const Problem& pr, const gemm_f16f32_opts* opts, Part* parts, int
   return GEMM_F16F32_OK;
 }
 
-template <int BM, int BN, int BK, int NS, bool AKM, bool BKM>
+template <int BM, int BN, int BK, int NS, int RD, int WM, int WN, bool AKM, bool BKM>
 hipError_t launch_layout(const gemm_f16f32_plan_info& r, const gk::Args& a, bool odd,
                          hipStream_t stream) {
-  const dim3 grid(r.num_programs), block(gk::kThreads);
+  const dim3 grid(r.num_programs), block(64 * WM * WN);
   if (r.path == GEMM_F16F32_PATH_DMA)
-    hipLaunchKernelGGL((gk::gemm_dma<BM, BN, BK, NS, AKM, BKM>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((gk::gemm_dma<BM, BN, BK, NS, RD, WM, WN, AKM, BKM>), grid, block, 0,
+                       stream, a);
   else if (odd)
-    hipLaunchKernelGGL((gk::gemm_generic<BM, BN, true, AKM, BKM>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((gk::gemm_generic<BM, BN, true, WM, WN, AKM, BKM>), grid, block, 0,
+                       stream, a);
   else
-    hipLaunchKernelGGL((gk::gemm_generic<BM, BN, false, AKM, BKM>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((gk::gemm_generic<BM, BN, false, WM, WN, AKM, BKM>), grid, block, 0,
+                       stream, a);
   return hipGetLastError();
 }
 
-template <int BM, int BN, int BK, int NS>
+// One tile configuration: BM x BN x BK, NS LDS stages, operands read RD k steps ahead,
+// WM x WN wavefronts.
+template <int BM, int BN, int BK, int NS, int RD, int WM, int WN>
 hipError_t launch(const gemm_f16f32_plan_info& r, const gk::Args& a, bool odd,
                   hipStream_t stream) {
   if (r.a_kmajor)
-    return r.b_kmajor ? launch_layout<BM, BN, BK, NS, true, true>(r, a, odd, stream)
-                      : launch_layout<BM, BN, BK, NS, true, false>(r, a, odd, stream);
-  return r.b_kmajor ? launch_layout<BM, BN, BK, NS, false, true>(r, a, odd, stream)
-                    : launch_layout<BM, BN, BK, NS, false, false>(r, a, odd, stream);
+    return r.b_kmajor
+               ? launch_layout<BM, BN, BK, NS, RD, WM, WN, true, true>(r, a, odd, stream)
+               : launch_layout<BM, BN, BK, NS, RD, WM, WN, true, false>(r, a, odd, stream);
+  return r.b_kmajor
+             ? launch_layout<BM, BN, BK, NS, RD, WM, WN, false, true>(r, a, odd, stream)
+             : launch_layout<BM, BN, BK, NS, RD, WM, WN, false, false>(r, a, odd, stream);
 }
 
 int launch_part(const Problem& pr, const Part& pt, hipStream_t s) {
@@ -258,13 +275,10 @@ int launch_part(const Problem& pr, const Part& pt, hipStream_t s) {
   const bool odd = (((uintptr_t)a.A | (uintptr_t)a.B) & 3) != 0 || ((pr.lda | pr.ldb) & 1) != 0;
   hipError_t e = hipSuccess;
   switch (r.tile) {
-    case GEMM_F16F32_TILE_256x256x64: e = launch<256, 256, 64, 2>(r, a, odd, s); break;
-    case GEMM_F16F32_TILE_256x128x64: e = launch<256, 128, 64, 2>(r, a, odd, s); break;
-    case GEMM_F16F32_TILE_128x128x64: e = launch<128, 128, 64, 2>(r, a, odd, s); break;
-    case GEMM_F16F32_TILE_128x64x64: e = launch<128, 64, 64, 2>(r, a, odd, s); break;
-    case GEMM_F16F32_TILE_256x256x32: e = launch<256, 256, 32, 4>(r, a, odd, s); break;
-    case GEMM_F16F32_TILE_64x64x32: e = launch<64, 64, 32, 5>(r, a, odd, s); break;
-    case GEMM_F16F32_TILE_128x64x32: e = launch<128, 64, 32, 5>(r, a, odd, s); break;
+#define GEMM_F16F32_TILE_CASE(id, bm, bn, bk, ns, rd, wm, wn, g) \
+  case id: e = launch<bm, bn, bk, ns, rd, wm, wn>(r, a, odd, s); break;
+    GEMM_F16F32_TILES(GEMM_F16F32_TILE_CASE)
+#undef GEMM_F16F32_TILE_CASE
     default: return GEMM_F16F32_ERR_OPTS;
   }
   return e == hipSuccess ? GEMM_F16F32_OK : GEMM_F16F32_ERR_HIP;

@@ -38,8 +38,8 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 #define GK_LDS __attribute__((address_space(3)))
 
 constexpr int kXcds = 8;       // MI355X: 8 XCDs, workgroups dealt round-robin
-constexpr int kThreads = 256;  // 4 wavefronts of 64 lanes in a 2 x 2 arrangement
-constexpr int kBK = 64;        // k depth of one staged panel
+constexpr int kBK = 64;        // k depth of one staged panel (generic path; the widest)
+constexpr int kMaxStages = 16; // LDS stages of the DMA path, at most
 
 struct Args {
   const uint16_t* A;
@@ -86,30 +86,35 @@ __device__ __forceinline__ void program_tile(int h, int P, int num_pid_m, int nu
 //    (ds_read_b64_tr_b16, 4 k rows each).
 // Chunk c of LDS row r sits at chunk position c ^ swz(r).
 // ---------------------------------------------------------------------------------------
-template <int BX_, int BK_, bool KM_>
+template <int BX_, int BK_, bool KM_, int W_, int NW_>
 struct Opnd {
   static constexpr int BX = BX_, BK = BK_;
   static constexpr bool KM = KM_;
+  static constexpr int W = W_;                       // waves along X
+  static constexpr int NW = NW_;                     // waves in the workgroup
   static constexpr int ROWS = KM ? BX : BK;          // LDS rows of one panel
   static constexpr int CH = (KM ? BK : BX) / 8;      // 16-byte chunks per LDS row
   static constexpr int ROW_BYTES = CH * 16;
   static constexpr int BYTES = BX * BK * 2;
-  static constexpr int LD = BYTES / (kThreads * 16); // 16-byte loads per thread per panel
-  static constexpr int WX = BX / 2;                  // extent of one wave's block along X
+  static constexpr int LD = BYTES / (NW * 64 * 16); // 16-byte loads per thread per panel
+  static constexpr int WX = BX / W;                  // extent of one wave's block along X
   static constexpr int T = WX / 32;                  // 32-wide MFMA blocks per wave
   static constexpr int NOFF = KM ? BK / 16 : T;      // per-lane LDS read offsets
   static constexpr int READS = KM ? T : 2 * T;       // LDS read instructions per k step
-  static_assert(T >= 1 && LD >= 1, "operand tile too small for 256 threads");
+  static_assert(T >= 1 && LD >= 1 && WX % 32 == 0, "operand tile too small for its waves");
   static_assert(!KM || CH == 8 || CH == 4, "k-major LDS rows hold 64 or 32 halves");
-  static_assert(KM || CH == 8 || CH == 16 || CH == 32, "x-major LDS rows hold 64-256 halves");
+  static_assert(KM || CH == 4 || CH == 8 || CH == 16 || CH == 32,
+                "x-major LDS rows hold 32-256 halves");
 };
 
-template <int BM_, int BN_, int BK_, bool AKM, bool BKM>
+// A BM x BN tile of C computed by WM x WN wavefronts, each owning a (BM/WM) x (BN/WN) block.
+template <int BM_, int BN_, int BK_, bool AKM, bool BKM, int WM_, int WN_>
 struct Tile {
-  using OA = Opnd<BM_, BK_, AKM>;
-  using OB = Opnd<BN_, BK_, BKM>;
+  static constexpr int WM = WM_, WN = WN_, NW = WM * WN, NT = 64 * NW;  // waves, threads
+  using OA = Opnd<BM_, BK_, AKM, WM, NW>;
+  using OB = Opnd<BN_, BK_, BKM, WN, NW>;
   static constexpr int BM = BM_, BN = BN_, BK = BK_;
-  static constexpr int WTM = BM / 2, WTN = BN / 2;   // per-wave block of C (2 x 2 waves)
+  static constexpr int WTM = BM / WM, WTN = BN / WN; // per-wave block of C
   static constexpr int TM = OA::T, TN = OB::T;       // 32x32 MFMA blocks per wave
   static constexpr int A_BYTES = OA::BYTES, B_BYTES = OB::BYTES;
   static constexpr int STAGE = A_BYTES + B_BYTES;
@@ -164,7 +169,8 @@ __device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t r, void
 //    swizzle and their addresses differ by a constant.
 //  * x-major: a transposing read covers 4 consecutive rows x 2 (16 lanes) or x 4 (32 lanes)
 //    consecutive chunks; the XOR values 0, 10, 4, 14 for r % 4 = 0..3 (masked to the row's
-//    chunk count) spread both footprints over distinct banks.
+//    chunk count) spread both footprints over distinct banks.  Rows of 4 chunks (64 bytes)
+//    need none: 4 consecutive rows already fill one 256-byte bank line.
 template <class O>
 __device__ __forceinline__ int swz(int r) {
   if constexpr (O::KM) {
@@ -172,6 +178,8 @@ __device__ __forceinline__ int swz(int r) {
       return (r & 7) ^ ((r >> 3) & 1);
     else
       return ((r >> 1) ^ (r >> 3)) & 3;
+  } else if constexpr (O::CH == 4) {
+    return 0;
   } else {
     return ((0xE4A0 >> (4 * (r & 3))) & 0xF) & (O::CH - 1);
   }
@@ -359,18 +367,18 @@ __device__ __forceinline__ void wait_vmcnt() {
 // ---------------------------------------------------------------------------------------
 // Operand loading for the DMA path.
 //
-// Load slot q = (i*4 + w)*64 + lane of a panel (thread q mod 256 owns it) holds the chunk at
-// position q % CH of LDS row q / CH, i.e. logical chunk (q % CH) ^ swz(row).  Relative to the
-// panel's corner in global memory that chunk starts 2 (row * ld + 8 chunk) bytes in, for
-// either storage order (an LDS row is an x row of a k-major operand, a k row of an x-major
-// one).
+// Load slot q = (i*NW + w)*64 + lane of a panel (NW waves; thread q mod 64 NW owns it) holds
+// the chunk at position q % CH of LDS row q / CH, i.e. logical chunk (q % CH) ^ swz(row).
+// Relative to the panel's corner in global memory that chunk starts 2 (row * ld + 8 chunk)
+// bytes in, for either storage order (an LDS row is an x row of a k-major operand, a k row
+// of an x-major one).
 // ---------------------------------------------------------------------------------------
 template <class O>
 __device__ __forceinline__ void slot_offsets(uint32_t (&off)[O::LD], int w, int lane,
                                              int64_t ld) {
 #pragma unroll
   for (int i = 0; i < O::LD; ++i) {
-    const int q = (i * 4 + w) * 64 + lane;
+    const int q = (i * O::NW + w) * 64 + lane;
     const int r = q / O::CH, c = (q % O::CH) ^ swz<O>(r);
     off[i] = 2u * ((uint32_t)r * (uint32_t)ld + (uint32_t)(c * 8));
   }
@@ -386,7 +394,7 @@ __device__ __forceinline__ void dma_panel(const uint16_t* ptr, int64_t ld, int64
   const __amdgpu_buffer_rsrc_t r = make_rsrc(ptr + (live ? e0 : 0), live ? 2 * (ext - e0) : 0);
 #pragma unroll
   for (int i = 0; i < O::LD; ++i)
-    buffer_load_lds16(r, (void GK_LDS*)(dst + (i * 4 + w) * 1024), off[i]);
+    buffer_load_lds16(r, (void GK_LDS*)(dst + (i * O::NW + w) * 1024), off[i]);
 }
 
 // Head panel at (x0, kofs), kofs < 0: the same slots, through registers, with k < 0 read as
@@ -400,7 +408,7 @@ __device__ __forceinline__ void head_load(u32x4 (&v)[O::LD], const uint16_t* ptr
   const __amdgpu_buffer_rsrc_t r = make_rsrc(ptr + e0, 2 * (ext - e0));
 #pragma unroll
   for (int i = 0; i < O::LD; ++i) {
-    const int q = (i * 4 + w) * 64 + lane;
+    const int q = (i * O::NW + w) * 64 + lane;
     const int row = q / O::CH, c = (q % O::CH) ^ swz<O>(row);
     if constexpr (O::KM) {
       uint16_t h[8];
@@ -426,7 +434,8 @@ template <class O>
 __device__ __forceinline__ void head_store(const u32x4 (&v)[O::LD], char GK_LDS* dst, int w,
                                            int lane) {
 #pragma unroll
-  for (int i = 0; i < O::LD; ++i) *(u32x4 GK_LDS*)(dst + ((i * 4 + w) * 64 + lane) * 16) = v[i];
+  for (int i = 0; i < O::LD; ++i)
+    *(u32x4 GK_LDS*)(dst + ((i * O::NW + w) * 64 + lane) * 16) = v[i];
 }
 
 // The operand's last element (X-1, K-1) in the last panel.  A 16-byte load that starts 2
@@ -449,7 +458,7 @@ __device__ __forceinline__ int last_element_slot(int x0, int X, int K, const uin
     q = (O::BK - 1) * O::CH + ((xl >> 3) ^ swz<O>(O::BK - 1));
     byte = (xl & 7) * 2;
   }
-  if ((q & (kThreads - 1)) != (int)threadIdx.x) return -1;
+  if ((q & (O::NW * 64 - 1)) != (int)threadIdx.x) return -1;
   value = __builtin_amdgcn_raw_buffer_load_b16(make_rsrc(ptr + ext - 1, 2), 0u, 0, 0);
   return q * 16 + byte;
 }
@@ -475,26 +484,28 @@ __device__ __forceinline__ int last_element_slot(int x0, int X, int K, const uin
 // resources: they load zeros, touch no memory and add exactly +0, which keeps the loop free
 // of branches.
 // ---------------------------------------------------------------------------------------
-template <int BM, int BN, int BK, int NS, bool AKM, bool BKM>
-__global__ void __launch_bounds__(kThreads) gemm_dma(Args p) {
-  using T = Tile<BM, BN, BK, AKM, BKM>;
+template <int BM, int BN, int BK, int NS, int RD, int WM, int WN, bool AKM, bool BKM>
+__global__ void __launch_bounds__(64 * WM * WN) gemm_dma(Args p) {
+  using T = Tile<BM, BN, BK, AKM, BKM, WM, WN>;
   using OA = typename T::OA;
   using OB = typename T::OB;
   constexpr int KS = BK / 16;              // k steps per panel
   constexpr int NM = T::TM * T::TN;        // MFMAs per k step
   constexpr int ND = OA::READS + OB::READS;  // LDS reads per k step
   constexpr int NV = T::A_LD + T::B_LD;    // buffer->LDS loads per panel
-  static_assert(KS % 2 == 0 && NS >= 2 && NS <= 5, "pipeline shape");
+  static_assert(KS % 2 == 0 && NS >= 2 && NS <= kMaxStages, "pipeline shape");
   static_assert(NS * T::STAGE <= 160 * 1024, "LDS");
-  __shared__ __attribute__((aligned(16))) char stage0[T::STAGE];
-  __shared__ __attribute__((aligned(16))) char stage1[T::STAGE];
-  __shared__ __attribute__((aligned(16))) char stage2[NS > 2 ? T::STAGE : 16];
-  __shared__ __attribute__((aligned(16))) char stage3[NS > 3 ? T::STAGE : 16];
-  __shared__ __attribute__((aligned(16))) char stage4[NS > 4 ? T::STAGE : 16];
+  static_assert((NS - 2) * NV <= 63, "vmcnt range");
+  static_assert(RD >= 1 && RD < KS && (NS * KS) % (RD + 1) == 0, "read-ahead distance");
+#define GK_STAGE(j) __shared__ __attribute__((aligned(16))) char stage##j[NS > j ? T::STAGE : 16];
+  GK_STAGE(0) GK_STAGE(1) GK_STAGE(2) GK_STAGE(3) GK_STAGE(4) GK_STAGE(5) GK_STAGE(6)
+  GK_STAGE(7) GK_STAGE(8) GK_STAGE(9) GK_STAGE(10) GK_STAGE(11) GK_STAGE(12) GK_STAGE(13)
+  GK_STAGE(14) GK_STAGE(15)
+#undef GK_STAGE
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wm = w >> 1, wn = w & 1;
+  const int wm = w / WN, wn = w % WN;
 
   int pid, pid_m, pid_n;
   program_tile(blockIdx.x, p.num_programs, p.num_pid_m, p.num_pid_n, p.group_m, p.xcd_remap,
@@ -543,43 +554,50 @@ __global__ void __launch_bounds__(kThreads) gemm_dma(Args p) {
     for (int tn = 0; tn < T::TN; ++tn)
       acc[tm][tn] = float16v{};
 
-  char GK_LDS* const S[5] = {(char GK_LDS*)stage0, (char GK_LDS*)stage1, (char GK_LDS*)stage2,
-                             (char GK_LDS*)stage3, (char GK_LDS*)stage4};
+  char GK_LDS* const S[kMaxStages] = {
+      (char GK_LDS*)stage0,  (char GK_LDS*)stage1,  (char GK_LDS*)stage2,  (char GK_LDS*)stage3,
+      (char GK_LDS*)stage4,  (char GK_LDS*)stage5,  (char GK_LDS*)stage6,  (char GK_LDS*)stage7,
+      (char GK_LDS*)stage8,  (char GK_LDS*)stage9,  (char GK_LDS*)stage10, (char GK_LDS*)stage11,
+      (char GK_LDS*)stage12, (char GK_LDS*)stage13, (char GK_LDS*)stage14, (char GK_LDS*)stage15};
   const LaneOffsets<T> lo = lane_offsets<T>(wm, wn, lane);
-  Frag<T> f[2];
+  // Operands are read RD k steps ahead of the MFMAs that use them: a ring of RD + 1
+  // fragments, indexed by the k step's position in the NS-panel unrolled loop.
+  Frag<T> f[RD + 1];
 
-  // One panel from stage `cur`, with panel s+1 in `nxt`; `prev` held panel s-1.
-  //  * NS == 2: past the barrier in the last k step, `cur` (just consumed) is refilled with
-  //    panel s+2.
+  // Panel s from stage `cur` (position j in the unrolled loop), with panel s+1 in `nxt`;
+  // `prev` held panel s-1.  K step kk multiplies the operands of step kk and reads those of
+  // step kk + RD, which from kk = KS - RD on lie in panel s+1: that is where this panel's
+  // barrier sits (after it every wave has read all of panel s, and panel s+1 has landed).
+  //  * NS == 2: right past the barrier, `cur` is refilled with panel s+2.
   //  * NS >= 3: `prev` is refilled with panel s+NS-1 at the start of the panel, its loads
   //    spread over the first k step's MFMAs.  Every wave finished reading `prev` before the
   //    previous panel's barrier (which waits for the wave's own LDS reads), so no further
   //    synchronisation is needed, and this panel's barrier only has to see panel s+1 land.
-  auto panel = [&](int s, char GK_LDS* cur, char GK_LDS* nxt, char GK_LDS* prev)
+  auto panel = [&](int s, int j, char GK_LDS* cur, char GK_LDS* nxt, char GK_LDS* prev)
                    __attribute__((always_inline)) {
 #pragma unroll
-    for (int kk = 0; kk + 1 < KS; ++kk) {
+    for (int kk = 0; kk < KS; ++kk) {
       if constexpr (NS >= 3) {
         if (kk == 0) issue(s + NS - 1, prev);
       }
-      read_frags<T>(f[(kk + 1) & 1], cur, lo, kk + 1);
-      mfma_step<T>(acc, f[kk & 1]);
-      if constexpr (NS >= 3) {
-        if (kk == 0)
-          sched_step<NM, ND, NV>();
-        else
-          sched_step<NM, ND, 0>();
-      } else {
-        sched_step<NM, ND, 0>();
+      if (kk == KS - RD) {
+        wait_vmcnt<(NS - 2) * NV>();   // panel s+1 has landed (this wave's part)
+        if (s + 2 == np) patch(nxt);   // panel s+1 is the last one
+        lds_barrier();                 // ... every wave's part
+        if constexpr (NS == 2) issue(s + NS, cur);
       }
+      const int ka = kk + RD;
+      if (ka < KS)
+        read_frags<T>(f[(j * KS + ka) % (RD + 1)], cur, lo, ka);
+      else
+        read_frags<T>(f[(j * KS + ka) % (RD + 1)], nxt, lo, ka - KS);
+      mfma_step<T>(acc, f[(j * KS + kk) % (RD + 1)]);
+      const bool loads = NS >= 3 ? kk == 0 : kk == KS - RD;
+      if (loads)
+        sched_step<NM, ND, NV>();
+      else
+        sched_step<NM, ND, 0>();
     }
-    wait_vmcnt<(NS - 2) * NV>();   // panel s+1 has landed (this wave's part)
-    if (s + 2 == np) patch(nxt);   // panel s+1 is the last one
-    lds_barrier();                 // ... every wave's part
-    if constexpr (NS == 2) issue(s + NS, cur);
-    read_frags<T>(f[0], nxt, lo, 0);
-    mfma_step<T>(acc, f[1]);
-    sched_step<NM, ND, NS == 2 ? NV : 0>();
   };
 
   if (np > 0) {
@@ -595,11 +613,13 @@ __global__ void __launch_bounds__(kThreads) gemm_dma(Args p) {
     wait_vmcnt<(kPre - 1) * NV>();
     if (np == 1) patch(S[0]);
     lds_barrier();
-    read_frags<T>(f[0], S[0], lo, 0);
+#pragma unroll
+    for (int d = 0; d < RD; ++d) read_frags<T>(f[d], S[0], lo, d);
   }
   for (int s = 0; s < np; s += NS) {
 #pragma unroll
-    for (int j = 0; j < NS; ++j) panel(s + j, S[j], S[(j + 1) % NS], S[(j + NS - 1) % NS]);
+    for (int j = 0; j < NS; ++j)
+      panel(s + j, j, S[j], S[(j + 1) % NS], S[(j + NS - 1) % NS]);
   }
   // The last refills (of panels past the end) must land before the workgroup's LDS is freed.
   wait_vmcnt<0>();
@@ -643,7 +663,7 @@ __device__ __forceinline__ u32x4 mask_k(u32x4 v, int first, int K) {
   return v;
 }
 
-// Slot q = i*256 + t of a panel holds logical chunk q % CH of LDS row q / CH.
+// Slot q = i*NT + t of a panel (NT threads) holds logical chunk q % CH of LDS row q / CH.
 template <class O, bool kOdd>
 __device__ __forceinline__ void generic_fetch(u32x4 (&v)[O::LD], const uint16_t* ptr,
                                               int64_t ld, int64_t ext, int x0, int k0, int K,
@@ -653,7 +673,7 @@ __device__ __forceinline__ void generic_fetch(u32x4 (&v)[O::LD], const uint16_t*
   const bool tail = k0 + O::BK > K;
 #pragma unroll
   for (int i = 0; i < O::LD; ++i) {
-    const int q = i * kThreads + t;
+    const int q = i * O::NW * 64 + t;
     const int row = q / O::CH, c = q % O::CH;
     v[i] = load_chunk<kOdd>(r, 2u * ((uint32_t)row * (uint32_t)ld + (uint32_t)(c * 8)));
     if constexpr (O::KM) {
@@ -667,14 +687,14 @@ __device__ __forceinline__ void generic_deposit(const u32x4 (&v)[O::LD], char GK
                                                 int t) {
 #pragma unroll
   for (int i = 0; i < O::LD; ++i) {
-    const int q = i * kThreads + t;
+    const int q = i * O::NW * 64 + t;
     *(u32x4 GK_LDS*)(dst + lds_chunk<O>(q / O::CH, q % O::CH)) = v[i];
   }
 }
 
-template <int BM, int BN, bool kOdd, bool AKM, bool BKM>
-__global__ void __launch_bounds__(kThreads) gemm_generic(Args p) {
-  using T = Tile<BM, BN, kBK, AKM, BKM>;
+template <int BM, int BN, bool kOdd, int WM, int WN, bool AKM, bool BKM>
+__global__ void __launch_bounds__(64 * WM * WN) gemm_generic(Args p) {
+  using T = Tile<BM, BN, kBK, AKM, BKM, WM, WN>;
   using OA = typename T::OA;
   using OB = typename T::OB;
   __shared__ __attribute__((aligned(16))) char smem[2 * T::STAGE];
@@ -682,7 +702,7 @@ __global__ void __launch_bounds__(kThreads) gemm_generic(Args p) {
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);
-  const int wm = w >> 1, wn = w & 1;
+  const int wm = w / WN, wn = w % WN;
 
   int pid, pid_m, pid_n;
   program_tile(blockIdx.x, p.num_programs, p.num_pid_m, p.num_pid_n, p.group_m, p.xcd_remap,

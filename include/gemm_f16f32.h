@@ -62,19 +62,25 @@ enum {
     GEMM_F16F32_ERR_HIP = -7        /* the HIP runtime rejected the launch */
 };
 
-/* Tile configurations (BM x BN x BK; 256 threads = 4 wavefronts of 64 lanes in a 2 x 2
- * arrangement, each accumulating a (BM/2) x (BN/2) block with 32x32x16 fp16 MFMAs).  BK is
- * the k depth of one LDS-staged panel of the DMA path (2 LDS stages at BK = 64, 4 or 5 at
- * BK = 32); the generic path stages 64-deep panels for every tile. */
+/* Tile configurations: BM x BN x BK, computed by a workgroup of wavefronts (64 lanes each)
+ * that each accumulate a block of C with 32x32x16 fp16 MFMAs.  Unless noted, 4 wavefronts in
+ * a 2 x 2 arrangement (256 threads).  BK is the k depth of one LDS-staged panel of the DMA
+ * path; the generic path stages 64-deep panels for every tile.  Every tile gives the same
+ * result bit for bit (each element's k-sum is the same sequence of MFMA steps). */
 enum {
     GEMM_F16F32_TILE_AUTO = 0,
-    GEMM_F16F32_TILE_256x256x64 = 1,
-    GEMM_F16F32_TILE_128x128x64 = 2,
-    GEMM_F16F32_TILE_128x64x64 = 3,
-    GEMM_F16F32_TILE_256x128x64 = 4,
-    GEMM_F16F32_TILE_256x256x32 = 5,
-    GEMM_F16F32_TILE_64x64x32 = 6,    /* 5 LDS stages */
-    GEMM_F16F32_TILE_128x64x32 = 7    /* 5 LDS stages */
+    GEMM_F16F32_TILE_256x256x64 = 1,     /* 2 LDS stages */
+    GEMM_F16F32_TILE_128x128x64 = 2,     /* 2 stages, operands read 3 k steps ahead */
+    GEMM_F16F32_TILE_128x64x64 = 3,      /* 2 stages */
+    GEMM_F16F32_TILE_256x128x64 = 4,     /* 2 stages, operands read 3 k steps ahead */
+    GEMM_F16F32_TILE_256x256x32 = 5,     /* 4 stages */
+    GEMM_F16F32_TILE_64x64x32 = 6,       /* 5 stages */
+    GEMM_F16F32_TILE_128x64x32 = 7,      /* 5 stages */
+    GEMM_F16F32_TILE_256x256x64_W8 = 8,  /* 8 wavefronts (2 x 4, 512 threads, two per SIMD) */
+    GEMM_F16F32_TILE_64x64x64 = 9,       /* 4 stages, read 3 ahead */
+    GEMM_F16F32_TILE_32x32x64 = 10,      /* 1 wavefront, 4 stages, read 3 ahead */
+    GEMM_F16F32_TILE_32x64x64 = 11,      /* 2 wavefronts (1 x 2), 4 stages, read 3 ahead */
+    GEMM_F16F32_TILE_64x32x64 = 12       /* 2 wavefronts (2 x 1), 4 stages, read 3 ahead */
 };
 
 /* Kernel families.  Both accept any shape, leading dimension and 2-byte alignment. */
@@ -120,6 +126,7 @@ typedef struct gemm_f16f32_plan_info {
     int32_t swapped;       /* 1: C is column-major and the launch computes C^T = B^T A^T; its
                               first operand is then B^T, and bm, num_pid_m, main_m run along
                               N, bn, num_pid_n, main_n along M */
+    int32_t threads;       /* workgroup size of the main launch */
 } gemm_f16f32_plan_info;
 
 /*

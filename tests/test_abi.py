@@ -76,7 +76,7 @@ def test_empty_problems_are_noops():
 
 def test_option_errors():
     base = (64, 64, 64, PA, PB, PC, 64, 64, 64)
-    for bad in ({"tile": 8}, {"group_m": -1}, {"xcd_remap": 3}, {"force_generic": 2},
+    for bad in ({"tile": max(g.TILES) + 1}, {"tile": -1}, {"group_m": -1}, {"xcd_remap": 3}, {"force_generic": 2},
                 {"split_edges": 3}):
         assert g.gemm_f16f32_plan(*base, opts=bad)[0] == g.ERR_OPTS
         assert g.gemm_f16f32_ex(*base, None, bad) == g.ERR_OPTS
