@@ -33,6 +33,7 @@ TILES = {TILE_256x256x64: (256, 256, 64, 256), TILE_128x128x64: (128, 128, 64, 2
 PATH_DMA, PATH_GENERIC = 0, 1
 REMAP_DEFAULT, REMAP_ON, REMAP_OFF = 0, 1, 2
 SPLIT_DEFAULT, SPLIT_ON, SPLIT_OFF = 0, 1, 2
+PERSISTENT_DEFAULT, PERSISTENT_ON, PERSISTENT_OFF = 0, 1, 2
 
 
 class GemmError(RuntimeError):
@@ -44,14 +45,15 @@ class GemmError(RuntimeError):
 class Opts(ctypes.Structure):
     _fields_ = [("tile", ctypes.c_int32), ("group_m", ctypes.c_int32),
                 ("xcd_remap", ctypes.c_int32), ("force_generic", ctypes.c_int32),
-                ("split_edges", ctypes.c_int32)]
+                ("split_edges", ctypes.c_int32), ("persistent", ctypes.c_int32)]
 
 
 class PlanInfo(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in ("path", "tile", "bm", "bn", "bk", "group_m",
                                               "xcd_remap", "num_pid_m", "num_pid_n",
                                               "num_programs", "launches", "main_m", "main_n",
-                                              "a_kmajor", "b_kmajor", "swapped", "threads")]
+                                              "a_kmajor", "b_kmajor", "swapped", "threads",
+                                              "persistent", "grid")]
 
     def as_dict(self) -> dict:
         return {n: getattr(self, n) for n, _ in self._fields_}

@@ -5,11 +5,14 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <cmath>
+
 #include "gemm_kernels.hpp"
 
 namespace {
 
-constexpr int kVersion = 200;  // 0.2.0
+constexpr int kVersion = 300;  // 0.3.0
+constexpr int kCUs = 256;       // compute units of an MI355X (the persistent grid's width)
 
 // The tile configurations: id, BM x BN x BK, NS LDS stages of the DMA kernel, operands read
 // RD k steps ahead, WM x WN wavefronts, default GROUP_SIZE_M.  (The generic kernel stages
@@ -44,16 +47,44 @@ const TileDesc* find_tile(int id) {
 
 int64_t cdiv(int64_t x, int64_t y) { return (x + y - 1) / y; }
 
-// Tile chosen from the shape: the largest tile whose grid still covers the 256 CUs about
-// once; smaller problems fall back to smaller tiles so that more CUs take part.  Thin shapes
-// (a side of at most 64) are latency bound over their whole K and take the 64 x 64 tile
-// with 32-deep panels and 5 LDS stages, which keeps 4 panels in flight.
-int auto_tile(int64_t M, int64_t N) {
+// Tile chosen from the shape when no table entry applies: the largest tile whose grid still
+// covers the 256 CUs about once; smaller problems fall back to smaller tiles so that more CUs
+// take part.  Thin shapes (a side of at most 64) are latency bound over their whole K and
+// take the 64 x 64 tile with 32-deep panels and 5 LDS stages, which keeps 4 panels in flight.
+int heuristic_tile(int64_t M, int64_t N) {
   if (cdiv(M, 256) * cdiv(N, 256) >= 240) return GEMM_F16F32_TILE_256x256x64;
   if (cdiv(M, 256) * cdiv(N, 128) >= 240) return GEMM_F16F32_TILE_256x128x64;
   if (cdiv(M, 128) * cdiv(N, 128) >= 120) return GEMM_F16F32_TILE_128x128x64;
   if (M <= 64 || N <= 64) return GEMM_F16F32_TILE_64x64x32;
   return GEMM_F16F32_TILE_128x64x64;
+}
+
+// The dispatch table measured offline by tune.py: for each shape class (rounded log2 of M,
+// N and K) the fastest tile and, where it mattered, GROUP_SIZE_M (0 = the tile's default).
+struct TuneEntry {
+  int8_t lm, ln, lk, tile, group;
+};
+constexpr TuneEntry kTune[] = {
+#include "tune_table.inc"
+    {-1, -1, -1, 0, 0}};  // end marker
+
+int log2_class(int64_t x, int lo, int hi) {
+  const int l = x < 1 ? lo : (int)std::lround(std::log2((double)x));
+  return l < lo ? lo : (l > hi ? hi : l);
+}
+
+struct Choice {
+  int tile, group;
+};
+
+// Tile and group size for an M x N x K launch: the table's entry for its shape class, else
+// the heuristic with the tile's default group size.
+Choice choose_tile(int64_t M, int64_t N, int64_t K) {
+  const int lm = log2_class(M, 5, 13), ln = log2_class(N, 5, 13), lk = log2_class(K, 6, 13);
+  for (const TuneEntry& e : kTune)
+    if (e.lm == lm && e.ln == ln && e.lk == lk && find_tile(e.tile) != nullptr)
+      return {e.tile, e.group};
+  return {heuristic_tile(M, N), 0};
 }
 
 // Bytes from a matrix's first element to one past its last, for rows x cols at leading
@@ -121,7 +152,7 @@ struct Part {
 };
 
 // Fills r for one launch of tile `tile` over M x N (no argument checks here).
-int plan_launch(const Problem& pr, int64_t M, int64_t N, const TileDesc* t,
+int plan_launch(const Problem& pr, int64_t M, int64_t N, const TileDesc* t, int group,
                 const gemm_f16f32_opts& o, gemm_f16f32_plan_info* r) {
   const int64_t kMax = (int64_t)1 << 31;
   // 32-bit in-kernel offsets: one panel's stored rows of A (bm rows if k-major, else up to 64
@@ -136,7 +167,7 @@ int plan_launch(const Problem& pr, int64_t M, int64_t N, const TileDesc* t,
   r->bn = t->bn;
   r->bk = dma ? t->bk : gk::kBK;
   r->threads = 64 * t->wm * t->wn;
-  r->group_m = o.group_m ? o.group_m : t->default_group;
+  r->group_m = o.group_m ? o.group_m : (group ? group : t->default_group);
   r->xcd_remap = (o.xcd_remap == 2) ? 0 : 1;
   const bool empty = (M == 0 || N == 0);
   r->num_pid_m = empty ? 0 : (int32_t)cdiv(M, t->bm);
@@ -144,6 +175,17 @@ int plan_launch(const Problem& pr, int64_t M, int64_t N, const TileDesc* t,
   const int64_t P = (int64_t)r->num_pid_m * r->num_pid_n;
   if (P >= kMax) return GEMM_F16F32_ERR_TOO_LARGE;
   r->num_programs = (int32_t)P;
+  // Persistent schedule (DMA path only): one round of workgroups over all CUs, as many per CU
+  // as fit in LDS, rounded down to a multiple of the 8 XCDs; never more than the programs.
+  r->persistent = dma && o.persistent == 1 && P > 0;
+  r->grid = (int32_t)P;
+  if (r->persistent) {
+    const int64_t lds = (int64_t)t->stages * (t->bm + t->bn) * t->bk * 2;
+    const int64_t per_cu = lds > 0 ? (160 * 1024) / lds : 1;
+    int64_t g = (int64_t)kCUs * (per_cu > 1 ? per_cu : 1);
+    g -= g % 8;
+    r->grid = (int32_t)(P < g ? P : g);
+  }
   r->launches = empty ? 0 : 1;
   r->main_m = (int32_t)M;
   r->main_n = (int32_t)N;
@@ -177,11 +219,12 @@ int plan_parts(const Problem& pr, const gemm_f16f32_opts* opts, Part* parts, int
   if (!emptyC && K > 0 && (pr.A == nullptr || pr.B == nullptr)) return GEMM_F16F32_ERR_NULL;
   if (((uintptr_t)pr.A | (uintptr_t)pr.B | (uintptr_t)pr.C) & 1) return GEMM_F16F32_ERR_OPTS;
 
-  gemm_f16f32_opts o = {0, 0, 0, 0, 0};
+  gemm_f16f32_opts o = {0, 0, 0, 0, 0, 0};
   if (opts) o = *opts;
   if (o.tile != 0 && find_tile(o.tile) == nullptr) return GEMM_F16F32_ERR_OPTS;
   if (o.group_m < 0 || o.xcd_remap < 0 || o.xcd_remap > 2 || o.force_generic < 0 ||
-      o.force_generic > 1 || o.split_edges < 0 || o.split_edges > 2)
+      o.force_generic > 1 || o.split_edges < 0 || o.split_edges > 2 || o.persistent < 0 ||
+      o.persistent > 2)
     return GEMM_F16F32_ERR_OPTS;
 
   if (!emptyC) {
@@ -192,7 +235,8 @@ int plan_parts(const Problem& pr, const gemm_f16f32_opts* opts, Part* parts, int
       return GEMM_F16F32_ERR_OVERLAP;
   }
 
-  const TileDesc* t = find_tile(o.tile ? o.tile : auto_tile(M, N));
+  const Choice ch = o.tile ? Choice{o.tile, 0} : choose_tile(M, N, K);
+  const TileDesc* t = find_tile(ch.tile);
   int64_t Mm = M, Nm = N;
   const bool split = o.split_edges == 1 || (o.split_edges == 0 && o.tile == 0);
   if (split && !emptyC) {
@@ -205,7 +249,7 @@ int plan_parts(const Problem& pr, const gemm_f16f32_opts* opts, Part* parts, int
   }
   Part* pp = parts;
   pp->m_off = 0, pp->n_off = 0, pp->M = Mm, pp->N = Nm;
-  int rc = plan_launch(pr, Mm, Nm, t, o, &pp->r);
+  int rc = plan_launch(pr, Mm, Nm, t, ch.group, o, &pp->r);
   if (rc != GEMM_F16F32_OK) return rc;
   ++pp;
   const int64_t strips[3][4] = {{0, Nm, Mm, N - Nm}, {Mm, 0, M - Mm, Nm}, {Mm, Nm, M - Mm, N - Nm}};
@@ -215,7 +259,8 @@ int plan_parts(const Problem& pr, const gemm_f16f32_opts* opts, Part* parts, int
   for (const auto& st : strips) {
     if (st[2] == 0 || st[3] == 0) continue;
     pp->m_off = st[0], pp->n_off = st[1], pp->M = st[2], pp->N = st[3];
-    rc = plan_launch(pr, st[2], st[3], find_tile(auto_tile(st[2], st[3])), os, &pp->r);
+    const Choice cs = choose_tile(st[2], st[3], K);
+    rc = plan_launch(pr, st[2], st[3], find_tile(cs.tile), cs.group, os, &pp->r);
     if (rc != GEMM_F16F32_OK) return rc;
     ++pp;
   }
@@ -227,8 +272,11 @@ int plan_parts(const Problem& pr, const gemm_f16f32_opts* opts, Part* parts, int
 template <int BM, int BN, int BK, int NS, int RD, int WM, int WN, bool AKM, bool BKM>
 hipError_t launch_layout(const gemm_f16f32_plan_info& r, const gk::Args& a, bool odd,
                          hipStream_t stream) {
-  const dim3 grid(r.num_programs), block(64 * WM * WN);
-  if (r.path == GEMM_F16F32_PATH_DMA)
+  const dim3 grid(r.grid), block(64 * WM * WN);
+  if (r.path == GEMM_F16F32_PATH_DMA && r.persistent)
+    hipLaunchKernelGGL((gk::gemm_dma_persistent<BM, BN, BK, NS, RD, WM, WN, AKM, BKM>), grid,
+                       block, 0, stream, a);
+  else if (r.path == GEMM_F16F32_PATH_DMA)
     hipLaunchKernelGGL((gk::gemm_dma<BM, BN, BK, NS, RD, WM, WN, AKM, BKM>), grid, block, 0,
                        stream, a);
   else if (odd)

@@ -447,7 +447,7 @@ __device__ __forceinline__ void head_store(const u32x4 (&v)[O::LD], char GK_LDS*
 // a stage (and its value), or -1 for every other thread.
 template <class O>
 __device__ __forceinline__ int last_element_slot(int x0, int X, int K, const uint16_t* ptr,
-                                                 int64_t ext, uint16_t& value) {
+                                                 int64_t ext, int tid, uint16_t& value) {
   const int xl = X - 1 - x0;
   if (K <= 0 || xl >= O::BX) return -1;
   int q, byte;
@@ -458,7 +458,7 @@ __device__ __forceinline__ int last_element_slot(int x0, int X, int K, const uin
     q = (O::BK - 1) * O::CH + ((xl >> 3) ^ swz<O>(O::BK - 1));
     byte = (xl & 7) * 2;
   }
-  if ((q & (O::NW * 64 - 1)) != (int)threadIdx.x) return -1;
+  if ((q & (O::NW * 64 - 1)) != tid) return -1;
   value = __builtin_amdgcn_raw_buffer_load_b16(make_rsrc(ptr + ext - 1, 2), 0u, 0, 0);
   return q * 16 + byte;
 }
@@ -484,8 +484,39 @@ __device__ __forceinline__ int last_element_slot(int x0, int X, int K, const uin
 // resources: they load zeros, touch no memory and add exactly +0, which keeps the loop free
 // of branches.
 // ---------------------------------------------------------------------------------------
+// The NS LDS stages of a DMA kernel: separate __shared__ objects (so that the compiler can
+// tell a refill of one stage from reads of another and does not wait for the refill), and
+// the array S of their addresses.
+#define GK_DECLARE_STAGES(NS, BYTES)                                                          \
+  __shared__ __attribute__((aligned(16))) char stage0[BYTES];                                 \
+  __shared__ __attribute__((aligned(16))) char stage1[BYTES];                                 \
+  __shared__ __attribute__((aligned(16))) char stage2[(NS) > 2 ? (BYTES) : 16];               \
+  __shared__ __attribute__((aligned(16))) char stage3[(NS) > 3 ? (BYTES) : 16];               \
+  __shared__ __attribute__((aligned(16))) char stage4[(NS) > 4 ? (BYTES) : 16];               \
+  __shared__ __attribute__((aligned(16))) char stage5[(NS) > 5 ? (BYTES) : 16];               \
+  __shared__ __attribute__((aligned(16))) char stage6[(NS) > 6 ? (BYTES) : 16];               \
+  __shared__ __attribute__((aligned(16))) char stage7[(NS) > 7 ? (BYTES) : 16];               \
+  __shared__ __attribute__((aligned(16))) char stage8[(NS) > 8 ? (BYTES) : 16];               \
+  __shared__ __attribute__((aligned(16))) char stage9[(NS) > 9 ? (BYTES) : 16];               \
+  __shared__ __attribute__((aligned(16))) char stage10[(NS) > 10 ? (BYTES) : 16];             \
+  __shared__ __attribute__((aligned(16))) char stage11[(NS) > 11 ? (BYTES) : 16];             \
+  __shared__ __attribute__((aligned(16))) char stage12[(NS) > 12 ? (BYTES) : 16];             \
+  __shared__ __attribute__((aligned(16))) char stage13[(NS) > 13 ? (BYTES) : 16];             \
+  __shared__ __attribute__((aligned(16))) char stage14[(NS) > 14 ? (BYTES) : 16];             \
+  __shared__ __attribute__((aligned(16))) char stage15[(NS) > 15 ? (BYTES) : 16];             \
+  char GK_LDS* const S[kMaxStages] = {                                                        \
+      (char GK_LDS*)stage0,  (char GK_LDS*)stage1,  (char GK_LDS*)stage2,                     \
+      (char GK_LDS*)stage3,  (char GK_LDS*)stage4,  (char GK_LDS*)stage5,                     \
+      (char GK_LDS*)stage6,  (char GK_LDS*)stage7,  (char GK_LDS*)stage8,                     \
+      (char GK_LDS*)stage9,  (char GK_LDS*)stage10, (char GK_LDS*)stage11,                    \
+      (char GK_LDS*)stage12, (char GK_LDS*)stage13, (char GK_LDS*)stage14,                    \
+      (char GK_LDS*)stage15};
+
+// One BM x BN tile of C with corner (m0, n0): the whole k loop and the store, on the LDS
+// stages S.
 template <int BM, int BN, int BK, int NS, int RD, int WM, int WN, bool AKM, bool BKM>
-__global__ void __launch_bounds__(64 * WM * WN) gemm_dma(Args p) {
+__device__ __forceinline__ void dma_tile(const Args& p, int m0, int n0,
+                                         char GK_LDS* const (&S)[kMaxStages]) {
   using T = Tile<BM, BN, BK, AKM, BKM, WM, WN>;
   using OA = typename T::OA;
   using OB = typename T::OB;
@@ -497,20 +528,15 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_dma(Args p) {
   static_assert(NS * T::STAGE <= 160 * 1024, "LDS");
   static_assert((NS - 2) * NV <= 63, "vmcnt range");
   static_assert(RD >= 1 && RD < KS && (NS * KS) % (RD + 1) == 0, "read-ahead distance");
-#define GK_STAGE(j) __shared__ __attribute__((aligned(16))) char stage##j[NS > j ? T::STAGE : 16];
-  GK_STAGE(0) GK_STAGE(1) GK_STAGE(2) GK_STAGE(3) GK_STAGE(4) GK_STAGE(5) GK_STAGE(6)
-  GK_STAGE(7) GK_STAGE(8) GK_STAGE(9) GK_STAGE(10) GK_STAGE(11) GK_STAGE(12) GK_STAGE(13)
-  GK_STAGE(14) GK_STAGE(15)
-#undef GK_STAGE
 
-  const int lane = threadIdx.x & 63;
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // The thread index passes through an empty asm so that nothing derived from it (LDS and
+  // global offsets) is hoisted out of a persistent tile loop, where it would stay live across
+  // the whole k loop and push the accumulators' registers into scratch.
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = w / WN, wn = w % WN;
-
-  int pid, pid_m, pid_n;
-  program_tile(blockIdx.x, p.num_programs, p.num_pid_m, p.num_pid_n, p.group_m, p.xcd_remap,
-               pid, pid_m, pid_n);
-  const int m0 = pid_m * BM, n0 = pid_n * BN;
 
   uint32_t offA[T::A_LD], offB[T::B_LD];
   slot_offsets<OA>(offA, w, lane, p.lda);
@@ -523,8 +549,8 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_dma(Args p) {
   const int kofs = rk ? rk - BK : 0;             // panel s covers k in [kofs + s BK, + BK)
 
   uint16_t last_a = 0, last_b = 0;
-  const int patch_a = last_element_slot<OA>(m0, p.M, p.K, p.A, extA, last_a);
-  const int patch_b = last_element_slot<OB>(n0, p.N, p.K, p.B, extB, last_b);
+  const int patch_a = last_element_slot<OA>(m0, p.M, p.K, p.A, extA, tid, last_a);
+  const int patch_b = last_element_slot<OB>(n0, p.N, p.K, p.B, extB, tid, last_b);
   auto patch = [&](char GK_LDS* base) __attribute__((always_inline)) {
     if (patch_a >= 0) *(uint16_t GK_LDS*)(base + patch_a) = last_a;
     if (patch_b >= 0) *(uint16_t GK_LDS*)(base + T::A_BYTES + patch_b) = last_b;
@@ -554,11 +580,6 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_dma(Args p) {
     for (int tn = 0; tn < T::TN; ++tn)
       acc[tm][tn] = float16v{};
 
-  char GK_LDS* const S[kMaxStages] = {
-      (char GK_LDS*)stage0,  (char GK_LDS*)stage1,  (char GK_LDS*)stage2,  (char GK_LDS*)stage3,
-      (char GK_LDS*)stage4,  (char GK_LDS*)stage5,  (char GK_LDS*)stage6,  (char GK_LDS*)stage7,
-      (char GK_LDS*)stage8,  (char GK_LDS*)stage9,  (char GK_LDS*)stage10, (char GK_LDS*)stage11,
-      (char GK_LDS*)stage12, (char GK_LDS*)stage13, (char GK_LDS*)stage14, (char GK_LDS*)stage15};
   const LaneOffsets<T> lo = lane_offsets<T>(wm, wn, lane);
   // Operands are read RD k steps ahead of the MFMAs that use them: a ring of RD + 1
   // fragments, indexed by the k step's position in the NS-panel unrolled loop.
@@ -621,9 +642,39 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_dma(Args p) {
     for (int j = 0; j < NS; ++j)
       panel(s + j, j, S[j], S[(j + 1) % NS], S[(j + NS - 1) % NS]);
   }
-  // The last refills (of panels past the end) must land before the workgroup's LDS is freed.
+  // The last refills (of panels past the end) must land before the workgroup's LDS is freed
+  // (or reused for another tile).
   wait_vmcnt<0>();
   store_tile<T>(p, acc, m0, n0, wm, wn, lane);
+}
+
+// One workgroup per program: hardware id -> program id -> tile.
+template <int BM, int BN, int BK, int NS, int RD, int WM, int WN, bool AKM, bool BKM>
+__global__ void __launch_bounds__(64 * WM * WN) gemm_dma(Args p) {
+  GK_DECLARE_STAGES(NS, (Tile<BM, BN, BK, AKM, BKM, WM, WN>::STAGE))
+  int pid, pid_m, pid_n;
+  program_tile(blockIdx.x, p.num_programs, p.num_pid_m, p.num_pid_n, p.group_m, p.xcd_remap,
+               pid, pid_m, pid_n);
+  dma_tile<BM, BN, BK, NS, RD, WM, WN, AKM, BKM>(p, pid_m * BM, pid_n * BN, S);
+}
+
+// Persistent grouped schedule: a grid of G workgroups (a multiple of 8, at most the number
+// of programs) in which workgroup h computes the tiles of programs h, h + G, h + 2G, ...
+// Each of those ids goes through the same map as a hardware id of the one-workgroup-per-
+// program launch -- and as G is a multiple of 8 it is dealt to the same XCD -- so every tile
+// is computed exactly once and, at any moment, the tiles in flight are those of consecutive
+// ids in the grouped order.  Every workgroup leaves the loop after at most
+// ceil(P / G) tiles.
+template <int BM, int BN, int BK, int NS, int RD, int WM, int WN, bool AKM, bool BKM>
+__global__ void __launch_bounds__(64 * WM * WN) gemm_dma_persistent(Args p) {
+  GK_DECLARE_STAGES(NS, (Tile<BM, BN, BK, AKM, BKM, WM, WN>::STAGE))
+  for (int v = blockIdx.x; v < p.num_programs; v += gridDim.x) {
+    int pid, pid_m, pid_n;
+    program_tile(v, p.num_programs, p.num_pid_m, p.num_pid_n, p.group_m, p.xcd_remap, pid,
+                 pid_m, pid_n);
+    dma_tile<BM, BN, BK, NS, RD, WM, WN, AKM, BKM>(p, pid_m * BM, pid_n * BN, S);
+    __syncthreads();   // every wave is done with the stages before the next tile's prologue
+  }
 }
 
 // ---------------------------------------------------------------------------------------

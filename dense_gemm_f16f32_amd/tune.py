@@ -1,0 +1,187 @@
+"""Offline sweep of tile configuration and GROUP_SIZE_M per shape class (runs on the GPU).
+
+The launch grid of a GEMM depends on its tile shape, and which tile (and which group size)
+is fastest depends on the problem's shape: the tutorial that the grouped order comes from
+leaves the block sizes to an autotuner keyed on M, N and K.  This script is that autotuner,
+run once, offline: for every shape class of a log2 grid it times each tile configuration
+of the library (forced through gemm_f16f32_ex options), then GROUP_SIZE_M in 1..32 for the
+winner when the grid is large enough for the order to matter, and writes the winners as a
+C table (csrc/tune_table.inc) that the library's planner looks up by rounded log2 of
+(M, N, K).
+
+Each timing is the device time per launch of a HIP graph holding n back-to-back launches on
+resident operands (uniform on [-0.5, 0.5), row-major, leading dimension = row length), so
+host launch overhead does not enter.  Every forced configuration must also reproduce the
+first configuration's bits (all tiles add the same MFMA k steps per element).
+
+    python -m dense_gemm_f16f32_amd.tune [--out PATH] [--quick]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import dense_gemm_f16f32_amd as g  # noqa: E402
+
+MN_GRID = [32, 64, 128, 256, 512, 1024, 2048, 4096, 8192]
+K_GRID = [64, 128, 256, 512, 1024, 2048, 4096, 8192]
+GROUPS = [1, 2, 4, 8, 16, 32]
+MARGIN = 0.03      # a new choice must be this much faster than the current one
+TABLE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc", "tune_table.inc")
+
+
+def graph_time_us(torch, fn, target_us=3000.0, reps=3):
+    """Median over `reps` replays of a graph of n launches of fn, per launch (us)."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(s)
+        fn()
+        b.record(s)
+        torch.cuda.synchronize()
+        est = max(a.elapsed_time(b) * 1e3, 1.0)
+    torch.cuda.current_stream().wait_stream(s)
+    n = int(max(3, min(64, target_us / est)))
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gr):
+        for _ in range(n):
+            fn()
+    gr.replay()
+    torch.cuda.synchronize()
+    res = []
+    for _ in range(reps):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        gr.replay()
+        b.record()
+        torch.cuda.synchronize()
+        res.append(a.elapsed_time(b) * 1e3 / n)
+    del gr
+    return sorted(res)[len(res) // 2]
+
+
+def programs(M, N, tile):
+    bm, bn = g.TILES[tile][:2]
+    return -(-M // bm) * -(-N // bn)
+
+
+def tune_shape(torch, M, N, K, quick=False):
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(M * 1000003 + N * 1009 + K)
+    A = (torch.rand((M, K), device="cuda", generator=gen) - 0.5).half().view(torch.int16)
+    B = (torch.rand((K, N), device="cuda", generator=gen) - 0.5).half().view(torch.int16)
+    C = torch.empty((M, N), dtype=torch.int16, device="cuda")
+    split_off = dict(split_edges=g.SPLIT_OFF)
+    times, ref = {}, None
+    for tile in sorted(g.TILES):
+        if quick and programs(M, N, tile) > 4096:
+            continue
+        opts = dict(tile=tile, **split_off)
+        t = graph_time_us(torch, lambda: g.matmul(A, B, C, **opts))
+        bits = C.cpu()
+        if ref is None:
+            ref = bits
+        elif not torch.equal(bits, ref):
+            raise RuntimeError(f"tile {tile} changed the result at {M}x{N}x{K}")
+        times[tile] = t
+    auto = graph_time_us(torch, lambda: g.matmul(A, B, C))
+    # the library's current choice (table or heuristic) stays unless another tile is clearly
+    # faster in this same sweep: timings of large shapes move by several percent with the
+    # chip's power state, and a table that flips on noise helps nobody
+    rc, cur = g.gemm_f16f32_plan(M, N, K, A.data_ptr(), B.data_ptr(), C.data_ptr(), K, N, N,
+                                 opts=split_off)
+    current = cur["tile"]
+    best = min(times, key=times.get)
+    if current in times and times[best] > (1.0 - MARGIN) * times[current]:
+        best = current
+    group, group_times = 0, {}
+    if programs(M, N, best) >= 128:
+        for G in GROUPS:
+            opts = dict(tile=best, group_m=G, **split_off)
+            group_times[G] = graph_time_us(torch, lambda: g.matmul(A, B, C, **opts))
+        gbest = min(group_times, key=group_times.get)
+        # keep the tile's default unless another group size is clearly faster
+        rc, info = g.gemm_f16f32_plan(M, N, K, A.data_ptr(), B.data_ptr(), C.data_ptr(), K, N,
+                                      N, opts=dict(tile=best))
+        default_g = info["group_m"]
+        if group_times[gbest] < (1.0 - MARGIN) * group_times.get(default_g, times[best]):
+            group = gbest
+    return {"M": M, "N": N, "K": K, "best_tile": best, "group_m": group, "current": current,
+            "us": {str(k): round(v, 2) for k, v in times.items()},
+            "group_us": {str(k): round(v, 2) for k, v in group_times.items()},
+            "auto_us": round(auto, 2)}
+
+
+def write_table(path, results, device):
+    lines = [
+        "// Tile configuration and GROUP_SIZE_M per shape class, written by",
+        "// dense_gemm_f16f32_amd/tune.py from device-time sweeps on " + device + ".",
+        "// Key: rounded log2 of M, N (32 .. 8192) and K (64 .. 8192); group 0 = the tile's",
+        "// default.  Columns: log2 M, log2 N, log2 K, tile, group; the comment gives the",
+        "// chosen configuration's time and the time of the choice it replaced (same sweep), us.",
+    ]
+    for r in results:
+        lm, ln, lk = (int(round(math.log2(r[x]))) for x in ("M", "N", "K"))
+        best_us = r["us"][str(r["best_tile"])]
+        if r["group_m"]:
+            best_us = r["group_us"][str(r["group_m"])]
+        was = r["us"].get(str(r.get("current")), r["auto_us"])
+        lines.append(f"{{{lm}, {ln}, {lk}, {r['best_tile']}, {r['group_m']}}},"
+                     f"  // {r['M']}x{r['N']}x{r['K']}: {best_us} (was {was})")
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--out", default=TABLE, help="table to write (C rows)")
+    ap.add_argument("--json", default=None, help="also write every timing as JSON here")
+    ap.add_argument("--quick", action="store_true", help="skip grids above 4096 workgroups")
+    ap.add_argument("--from-json", default=None,
+                    help="only rewrite the table from a JSON file of an earlier sweep")
+    args = ap.parse_args()
+    if args.from_json:
+        with open(args.from_json) as f:
+            rec = json.load(f)
+        write_table(args.out, rec["results"], rec["device"])
+        print(f"wrote {args.out} ({len(rec['results'])} shape classes)")
+        return
+    import torch
+
+    torch.cuda.set_device(0)
+    props = torch.cuda.get_device_properties(0)
+    device = f"{props.name} ({getattr(props, 'gcnArchName', 'gfx950').split(':')[0]}, " \
+             f"{props.multi_processor_count} CUs)"
+    results = []
+    t0 = time.time()
+    for K in K_GRID:
+        for M in MN_GRID:
+            for N in MN_GRID:
+                r = tune_shape(torch, M, N, K, args.quick)
+                results.append(r)
+                print(json.dumps({k: r[k] for k in ("M", "N", "K", "best_tile", "group_m",
+                                                    "auto_us")}
+                                 | {"best_us": r["us"][str(r["best_tile"])],
+                                    "elapsed_s": round(time.time() - t0, 1)}), flush=True)
+    write_table(args.out, results, device)
+    if args.json:
+        with open(args.json, "w") as f:
+            json.dump({"device": device, "results": results}, f)
+    print(f"wrote {args.out} ({len(results)} shape classes)", flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -103,6 +103,10 @@ typedef struct gemm_f16f32_opts {
                               columns (or the last tile row <= 1/4 of its rows) and the rest
                               spans >= 128 tiles, that sliver is computed by separate launches
                               with tiles sized for it; results are unchanged. */
+    int32_t persistent;    /* 0 = default (off), 1 = persistent grouped schedule: the DMA path
+                              launches one round of workgroups (256 CUs x as many per CU as fit
+                              in LDS, a multiple of 8) and workgroup h computes programs h,
+                              h + grid, ... through the same map; results are unchanged. 2 = off */
 } gemm_f16f32_opts;
 
 /* What a call with these arguments would launch (filled by gemm_f16f32_plan).  The fields
@@ -127,6 +131,8 @@ typedef struct gemm_f16f32_plan_info {
                               first operand is then B^T, and bm, num_pid_m, main_m run along
                               N, bn, num_pid_n, main_n along M */
     int32_t threads;       /* workgroup size of the main launch */
+    int32_t persistent;    /* 1 if the main launch uses the persistent schedule */
+    int32_t grid;          /* workgroups of the main launch (num_programs unless persistent) */
 } gemm_f16f32_plan_info;
 
 /*

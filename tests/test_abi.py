@@ -8,6 +8,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 import dense_gemm_f16f32_amd as g
@@ -97,23 +98,74 @@ def plan(M, N, K, lda=None, ldb=None, ldc=None, a=PA, b=PB, c=PC, **opts):
     return info
 
 
+TUNE_TABLE = os.path.join(ROOT, "dense_gemm_f16f32_amd", "csrc", "tune_table.inc")
+
+
+def tune_entries():
+    """(log2 M, log2 N, log2 K) -> (tile, group) rows of the compiled dispatch table."""
+    rows = {}
+    for ln in open(TUNE_TABLE):
+        m = re.match(r"\s*\{(-?\d+), (-?\d+), (-?\d+), (\d+), (\d+)\}", ln)
+        if m:
+            lm, lnn, lk, tile, grp = map(int, m.groups())
+            rows[(lm, lnn, lk)] = (tile, grp)
+    return rows
+
+
+def shape_class(M, N, K):
+    def c(x, lo, hi):
+        return min(max(lo if x < 1 else int(round(np.log2(x))), lo), hi)
+    return c(M, 5, 13), c(N, 5, 13), c(K, 6, 13)
+
+
+def expected_choice(M, N, K):
+    """The table's (tile, group) for this shape class, or None (heuristic)."""
+    return tune_entries().get(shape_class(M, N, K))
+
+
+def test_tune_table_rows_are_valid():
+    rows = tune_entries()
+    for key, (tile, grp) in rows.items():
+        assert tile in g.TILES and 0 <= grp <= 64, key
+        assert 5 <= key[0] <= 13 and 5 <= key[1] <= 13 and 6 <= key[2] <= 13, key
+
+
+def test_planner_follows_the_table():
+    for (lm, ln, lk), (tile, grp) in sorted(tune_entries().items()):
+        M, N, K = 1 << lm, 1 << ln, 1 << lk
+        p = plan(M, N, K)
+        assert p["tile"] == tile, (M, N, K)
+        want_g = grp or plan(M, N, K, tile=tile)["group_m"]
+        assert p["group_m"] == want_g, (M, N, K)
+        # a non-power-of-two shape in the same class gets the same tile
+        p2 = plan(M + M // 8, N, K)
+        if shape_class(M + M // 8, N, K) == (lm, ln, lk) and p2["launches"] == 1:
+            assert p2["tile"] == tile
+
+
 def test_plans_for_the_five_workloads():
-    p = plan(512, 512, 512)
-    assert (p["path"], p["bm"], p["bn"], p["num_programs"]) == (g.PATH_DMA, 128, 64, 32)
+    for M, N, K in [(512, 512, 512), (4096, 4096, 4096), (8192, 8192, 8192)]:
+        p = plan(M, N, K)
+        bm, bn = g.TILES[p["tile"]][:2]
+        assert p["path"] == g.PATH_DMA and (p["bm"], p["bn"]) == (bm, bn)
+        assert p["num_programs"] == -(-M // bm) * -(-N // bn)
+        want = expected_choice(M, N, K)
+        if want:
+            assert p["tile"] == want[0]
+    # the pages' worked example, forced: 128 x 64 tiles with G = 2
     p = plan(1024, 768, 128, tile=g.TILE_128x64x64, group_m=2)
     assert (p["num_pid_m"], p["num_pid_n"], p["num_programs"], p["group_m"]) == (8, 12, 96, 2)
-    p = plan(4096, 4096, 4096)
-    assert (p["path"], p["bm"], p["bn"], p["num_programs"]) == (g.PATH_DMA, 256, 256, 256)
-    p = plan(8192, 8192, 8192)
-    assert (p["path"], p["bm"], p["bn"], p["num_programs"]) == (g.PATH_DMA, 256, 256, 1024)
-    assert p["xcd_remap"] == 1
-    p = plan(4095, 4097, 4093, group_m=6)
-    # the 1-column sliver is split off: the main launch covers 4095 x 4096 with 16 x 16 tiles
+    assert plan(8192, 8192, 8192)["xcd_remap"] == 1
+    # ragged, 256 x 256 tiles: the 1-column sliver is split off, the main launch covers
+    # 4095 x 4096 with 16 x 16 tiles
+    p = plan(4095, 4097, 4093, tile=g.TILE_256x256x64, group_m=6, split_edges=g.SPLIT_ON)
     assert (p["path"], p["num_pid_m"], p["num_pid_n"], p["num_programs"]) == \
         (g.PATH_DMA, 16, 16, 256)
     assert (p["launches"], p["main_m"], p["main_n"]) == (2, 4095, 4096)
-    p = plan(4095, 4097, 4093, group_m=6, split_edges=g.SPLIT_OFF)
+    p = plan(4095, 4097, 4093, tile=g.TILE_256x256x64, group_m=6)
     assert (p["num_pid_m"], p["num_pid_n"], p["num_programs"], p["launches"]) == (16, 17, 272, 1)
+    p = plan(4095, 4097, 4093)
+    assert p["launches"] == 2 and p["main_n"] == 4096
 
 
 def test_path_selection():
@@ -141,12 +193,19 @@ def test_path_selection():
     (1000, 1001, (1, 1000, 1001)),        # small: fewer than 128 full tiles, kept
 ])
 def test_edge_split_plans(M, N, want):
-    p = plan(M, N, 512)
+    """With 256 x 256 tiles: slivers of at most a quarter tile are split off."""
+    p = plan(M, N, 512, tile=g.TILE_256x256x64, split_edges=g.SPLIT_ON)
     assert (p["launches"], p["main_m"], p["main_n"]) == want
     assert plan(M, N, 512, split_edges=g.SPLIT_OFF)["launches"] == 1
     # a forced tile splits only when asked
     assert plan(M, N, 512, tile=g.TILE_256x256x64)["launches"] == 1
-    assert plan(M, N, 512, tile=g.TILE_256x256x64, split_edges=g.SPLIT_ON)["launches"] >= 1
+    # a library-chosen tile splits by default, by the same rule for its own tile size
+    p = plan(M, N, 512)
+    bm, bn = p["bm"], p["bn"]
+    rm, rn = M % bm, N % bn
+    big = (M // bm) * (N // bn) >= 128
+    want_split = big and ((0 < rn and 4 * rn <= bn) or (0 < rm and 4 * rm <= bm))
+    assert (p["launches"] > 1) == want_split
 
 
 # ---- strided entry points ------------------------------------------------------------------
@@ -176,12 +235,17 @@ def test_strided_layouts(a_col, b_col, c_col):
     assert rc == g.OK
     if not c_col:
         assert (p["a_kmajor"], p["b_kmajor"], p["swapped"]) == (1 - a_col, b_col, 0)
-        assert (p["num_pid_m"], p["num_pid_n"]) == (-(-M // p["bm"]), -(-N // p["bn"]))
+        rows, cols = M, N
     else:
         # C^T = B^T A^T: first operand B^T is k-major iff B is column-major, A^T iff A is
         # row-major; the launch's rows run along N
         assert (p["a_kmajor"], p["b_kmajor"], p["swapped"]) == (b_col, 1 - a_col, 1)
-        assert (p["num_pid_m"], p["num_pid_n"]) == (-(-N // p["bm"]), -(-M // p["bn"]))
+        rows, cols = N, M
+    # the main launch covers all rows (columns), or all but an edge sliver split off
+    assert p["main_m"] in (rows, rows - rows % p["bm"])
+    assert p["main_n"] in (cols, cols - cols % p["bn"])
+    assert (p["num_pid_m"], p["num_pid_n"]) == (-(-p["main_m"] // p["bm"]),
+                                                -(-p["main_n"] // p["bn"]))
 
 
 @pytest.mark.parametrize("sa,sb,sc", [
@@ -220,11 +284,31 @@ def test_strided_overlap_uses_the_storage_footprint():
 
 
 def test_too_large_c_leading_dimension():
-    # 64 rows of C at ldc = 2^25 reach 2^31 elements: beyond the store offsets
+    # 64 rows of C (the 64 x 64 tile) at ldc = 2^25 reach 2^31 elements: beyond the store
+    # offsets
+    t64 = {"tile": g.TILE_64x64x32}
     args = (256, 8, 8, 1 << 40, 2 << 40, 3 << 40, 8, 8, 1 << 25)
-    assert g.gemm_f16f32_plan(*args)[0] == g.ERR_TOO_LARGE
+    assert g.gemm_f16f32_plan(*args, opts=t64)[0] == g.ERR_TOO_LARGE
     args = (256, 8, 8, 1 << 40, 2 << 40, 3 << 40, 8, 8, 1 << 24)
-    assert g.gemm_f16f32_plan(*args)[0] == g.OK
+    assert g.gemm_f16f32_plan(*args, opts=t64)[0] == g.OK
+    assert g.gemm_f16f32_plan(*args, opts={"tile": g.TILE_256x256x64})[0] == g.ERR_TOO_LARGE
     # a transposed operand's panel spans 64 k rows: 64 x lda
     assert splan(8, 8, 8, (1, 1 << 25), (8, 1), (8, 1), a=1 << 40, b=2 << 40,
                  c=3 << 40)[0] == g.ERR_TOO_LARGE
+
+
+def test_persistent_plans():
+    # one round of workgroups: 256 CUs x per-CU LDS fit, a multiple of 8, at most P
+    p = plan(8192, 8192, 8192, tile=g.TILE_256x256x64, persistent=g.PERSISTENT_ON)
+    assert p["persistent"] == 1 and p["grid"] == 256 and p["num_programs"] == 1024
+    p = plan(8192, 8192, 8192, tile=g.TILE_64x64x64, persistent=g.PERSISTENT_ON)
+    assert p["grid"] == 256 * 2 and p["num_programs"] == 128 * 128     # 64 KiB of LDS each
+    p = plan(512, 512, 512, tile=g.TILE_256x256x64, persistent=g.PERSISTENT_ON)
+    assert p["grid"] == p["num_programs"] == 4
+    p = plan(8192, 8192, 8192, tile=g.TILE_256x256x64)
+    assert p["persistent"] == 0 and p["grid"] == p["num_programs"]
+    # the generic path has no persistent form
+    p = plan(8192, 8192, 8192, persistent=g.PERSISTENT_ON, force_generic=1)
+    assert p["persistent"] == 0 and p["grid"] == p["num_programs"]
+    assert g.gemm_f16f32_plan(8, 8, 8, PA, PB, PC, 8, 8, 8, opts={"persistent": 3})[0] == \
+        g.ERR_OPTS

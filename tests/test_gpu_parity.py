@@ -328,3 +328,28 @@ def test_graph_capture_replays_match_eager():
         assert np.array_equal(from_dev(Cg), eager), rep
         other = from_dev(run(Ad, Bd, 500, 600, K))   # unrelated eager work in between
         assert_within_tolerance(other, eager[:500, :600], "eager between replays")
+
+
+@pytest.mark.parametrize("M,N,K,tile", [
+    (2048, 2048, 2048, g.TILE_256x256x64),          # fewer programs than the grid
+    (8192, 4096, 512, g.TILE_256x256x64),           # 512 programs on 256 workgroups
+    (8192, 4096, 512, g.TILE_256x256x64_W8),
+    (2048, 2048, 1000, g.TILE_64x64x64),            # 1024 programs on 512 workgroups
+    (3000, 1000, 700, g.TILE_32x32x64),             # 2976 programs, ragged, 5 per CU
+    (4095, 4097, 4093, 0),                          # library's choice, with the edge split
+])
+def test_persistent_schedule_changes_no_bit(M, N, K, tile):
+    """Workgroup h of the persistent grid computes programs h, h + grid, ...: every tile once,
+    with the same k order, so the result equals the one-workgroup-per-program launch."""
+    A, B = operands(M, N, K, "u(-0.5,0.5)", M + N + K)
+    Ad, Bd = to_dev(A), to_dev(B)
+    opts = dict(tile=tile) if tile else {}
+    rc, info = g.gemm_f16f32_plan(M, N, K, 1 << 40, 2 << 40, 3 << 40, K, N, N,
+                                  opts=dict(opts, persistent=g.PERSISTENT_ON))
+    assert rc == g.OK and info["persistent"] == 1 and info["grid"] <= info["num_programs"]
+    Cd = torch.full((M, N), 0x7E00, dtype=torch.int16, device="cuda")
+    plain = from_dev(run(Ad, Bd, M, N, K, **opts))
+    pers = from_dev(run(Ad, Bd, M, N, K, C_dev=Cd, persistent=g.PERSISTENT_ON, **opts))
+    assert np.array_equal(plain, pers)
+    r, c = sample_positions(M, N, 512, 512, 2, 3)
+    assert_within_tolerance(pers[r, c], oracle.gemm_sampled(A, B, r, c), f"{M}x{N}x{K}")
