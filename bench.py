@@ -13,7 +13,8 @@ HIP events recorded on the stream the kernel is launched on (torch's current str
 2 M N K / (mean per-launch event time), against the MI355X published dense fp16 matrix
 peak of 2.5 PFLOP/s.  `cpu_baseline` times the CPU oracle (fp64 ascending-k sums, one
 rounding) on one 256-row band of the same product, using all host threads it gets.
---all prints one extra JSON line per workload to stderr.  --layout stores A, B (and C) row-
+--all prints one extra JSON line per workload to stderr, with the device time per launch
+from HIP-graph replays beside the per-launch event times.  --layout stores A, B (and C) row-
 major ("n") or column-major ("t"), e.g. "nt" for B given as an N x K matrix; --layouts times
 all eight storage orders (stderr).
 """
@@ -126,6 +127,33 @@ def time_workload(g, torch, name, steps, warmup, opts, layout="nn"):
     }
 
 
+def graph_device_us(torch, fn, n=20, reps=5):
+    """Device time per launch (us) of fn, from replays of a HIP graph of n launches: the host
+    launch cost, which per-launch events see for kernels of a few microseconds, drops out."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for _ in range(3):
+            fn()
+    torch.cuda.current_stream().wait_stream(s)
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gr):
+        for _ in range(n):
+            fn()
+    gr.replay()
+    torch.cuda.synchronize()
+    res = []
+    for _ in range(reps):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        gr.replay()
+        b.record()
+        torch.cuda.synchronize()
+        res.append(a.elapsed_time(b) * 1e3 / n)
+    return sorted(res)[len(res) // 2]
+
+
 def time_torch(torch, name, steps, warmup):
     """torch.matmul (the vendor BLAS) on the same fp16 operands, for context only."""
     from synthetic_inputs import workload
@@ -232,6 +260,11 @@ def main():
             small = w[1] * w[2] * w[3] < 1 << 31
             r = time_workload(g, torch, w[0], 1000 if small else 50, 10, opts)
             r["frac_of_peak"] = r["achieved_tflops"] / PEAK_TFLOPS
+            Ad, Bd, Cd = device_operands(torch, w[0])
+            us = graph_device_us(torch, lambda: g.matmul(Ad, Bd, Cd, **opts),
+                                 n=50 if small else 5)
+            r["graph_us_per_launch"] = round(us, 3)
+            r["graph_tflops"] = round(2.0 * w[1] * w[2] * w[3] / us / 1e6, 1)
             print(json.dumps(r), file=sys.stderr, flush=True)
 
     if args.sweep:
