@@ -38,8 +38,13 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
 def kernel_source_hash() -> str:
+    """sha256 (first 16 hex digits) of the kernel and launch sources (csrc/*.hip, *.hpp).  The
+    dispatch table (tune_table.inc) is left out: it picks the launch configuration, which the
+    traffic record's key already names, and changes no kernel."""
     h = hashlib.sha256()
     for name in sorted(os.listdir(CSRC)):
+        if not name.endswith((".hip", ".hpp")):
+            continue
         with open(os.path.join(CSRC, name), "rb") as f:
             h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
