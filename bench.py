@@ -37,14 +37,15 @@ CSRC = os.path.join(ROOT, "dense_gemm_f16f32_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
+KERNEL_SOURCES = ("gemm_kernels.hpp", "gemm_tiles.hpp")
+
+
 def kernel_source_hash() -> str:
-    """sha256 (first 16 hex digits) of the kernel and launch sources (csrc/*.hip, *.hpp).  The
-    dispatch table (tune_table.inc) is left out: it picks the launch configuration, which the
-    traffic record's key already names, and changes no kernel."""
+    """sha256 (first 16 hex digits) of the files that fix the kernels' code: the device code
+    and the tile configurations.  The planner and its dispatch table are left out: they choose
+    the launch configuration, which the traffic record's key already names."""
     h = hashlib.sha256()
-    for name in sorted(os.listdir(CSRC)):
-        if not name.endswith((".hip", ".hpp")):
-            continue
+    for name in KERNEL_SOURCES:
         with open(os.path.join(CSRC, name), "rb") as f:
             h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]

@@ -312,3 +312,17 @@ def test_persistent_plans():
     assert p["persistent"] == 0 and p["grid"] == p["num_programs"]
     assert g.gemm_f16f32_plan(8, 8, 8, PA, PB, PC, 8, 8, 8, opts={"persistent": 3})[0] == \
         g.ERR_OPTS
+
+
+def test_misaligned_rows_take_the_eight_wavefront_tile():
+    """Where the table picks the 4-wavefront 256 x 256 tile for aligned rows, misaligned rows
+    (odd leading dimension or a 2-byte aligned start) get the 8-wavefront one."""
+    M = N = K = 4096
+    p = plan(M, N, K)
+    if p["tile"] != g.TILE_256x256x64:
+        pytest.skip("the table does not pick the 4-wavefront 256 x 256 tile here")
+    assert plan(M, N, K, lda=K + 1)["tile"] == g.TILE_256x256x64_W8
+    assert plan(M, N, K, ldb=N + 1)["tile"] == g.TILE_256x256x64_W8
+    assert plan(M, N, K, a=PA + 2)["tile"] == g.TILE_256x256x64_W8
+    assert plan(M, N, K, lda=K + 8)["tile"] == g.TILE_256x256x64
+    assert plan(4095, 4097, 4093)["tile"] == g.TILE_256x256x64_W8
