@@ -200,6 +200,121 @@ def copy_calibration(torch, mib, steps):
                       "GB_per_s": round(2 * n / dt / 1e9, 1)}), flush=True)
 
 
+def gfx_clocks_mhz():
+    """Current GFX clock of every XCD from `amd-smi metric -c` (empty list if unavailable)."""
+    import re
+    import subprocess
+    try:
+        out = subprocess.run(["amd-smi", "metric", "-c"], capture_output=True, text=True,
+                             timeout=10).stdout
+    except (OSError, subprocess.SubprocessError):
+        return []
+    clocks, in_gfx = [], False
+    for line in out.splitlines():
+        if re.match(r"\s*GFX_\d+:\s*$", line):
+            in_gfx = True
+            continue
+        m = re.match(r"\s*CLK:\s*(\d+)", line)
+        if in_gfx and m:
+            clocks.append(int(m.group(1)))
+            in_gfx = False
+        elif line.strip().endswith(":"):
+            in_gfx = False
+    return clocks
+
+
+def sample_clocks(g, torch, fn, seconds=3.0):
+    """Runs fn back to back for `seconds` (untimed, after the timed region) while sampling the
+    XCD clocks; returns min / median / max MHz over all samples and XCDs, or None."""
+    import threading
+    samples, done = [], threading.Event()
+
+    def poll():
+        while not done.is_set():
+            samples.extend(gfx_clocks_mhz())
+            time.sleep(0.2)
+
+    if not gfx_clocks_mhz():
+        return None
+    for _ in range(20):          # the clocks ramp up before sampling starts
+        fn()
+    torch.cuda.synchronize()
+    th = threading.Thread(target=poll, daemon=True)
+    t_end = time.perf_counter() + seconds
+    th.start()
+    prev = None
+    while time.perf_counter() < t_end:
+        for _ in range(20):
+            fn()
+        ev = torch.cuda.Event()
+        ev.record()
+        if prev is not None:     # one batch stays queued, so the GPU never idles
+            prev.synchronize()
+        prev = ev
+    done.set()
+    th.join()
+    torch.cuda.synchronize()
+    if not samples:
+        return None
+    samples.sort()
+    q = lambda f: samples[min(len(samples) - 1, int(f * len(samples)))]
+    # an XCD occasionally reads a few hundred MHz for an instant; percentiles keep such
+    # outliers from standing for the run
+    return {"p05": q(0.05), "median": q(0.5), "p95": q(0.95), "samples": len(samples)}
+
+
+def cpu_all():
+    """The oracle on every workload (one JSON line each): all threads, plus one thread on the
+    two small workloads; the large ones on a 256-row band.  Records the host CPU."""
+    import numpy as np
+    import oracle
+    from synthetic_inputs import WORKLOADS, operands
+
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next(ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name"))
+    except (OSError, StopIteration):
+        pass
+    oracle.lib()
+    for name, M, N, K, dist, seed in WORKLOADS:
+        A, B = operands(M, N, K, dist, seed)
+        rows = M if M * N * K <= 1 << 31 else min(256, M)
+        Ab = np.ascontiguousarray(A[:rows])
+        res = {"workload": name, "rows": rows, "N": N, "K": K, "cpu": model,
+               "nproc": os.cpu_count()}
+        t0 = time.perf_counter()
+        oracle.gemm(Ab, B)
+        dt = time.perf_counter() - t0
+        res["all_threads"] = {"s": round(dt, 4), "threads": oracle.num_threads(),
+                              "GFLOP/s": round(2.0 * rows * N * K / dt / 1e9, 2)}
+        if rows == M:
+            dt1 = _oracle_single_thread_seconds(Ab, B)
+            res["single_thread"] = {"s": round(dt1, 4), "threads": 1,
+                                    "GFLOP/s": round(2.0 * rows * N * K / dt1 / 1e9, 2)}
+        print(json.dumps(res), flush=True)
+
+
+def _oracle_single_thread_seconds(A, B):
+    """Seconds of one oracle GEMM on one host thread, timed inside a child process (OpenMP's
+    thread count is fixed once the library is loaded in this one)."""
+    import subprocess
+    import tempfile
+
+    import numpy as np
+    with tempfile.TemporaryDirectory() as d:
+        pa, pb = os.path.join(d, "a.npy"), os.path.join(d, "b.npy")
+        np.save(pa, A)
+        np.save(pb, B)
+        code = ("import sys, time, numpy as np; sys.path.insert(0, %r); import oracle; "
+                "a, b = np.load(%r), np.load(%r); oracle.lib(); t = time.perf_counter(); "
+                "oracle.gemm(a, b); print(time.perf_counter() - t)" % (ROOT, pa, pb))
+        env = dict(os.environ, OMP_NUM_THREADS="1")
+        out = subprocess.run([sys.executable, "-c", code], env=env, check=True,
+                             capture_output=True, text=True).stdout
+    return float(out.strip().splitlines()[-1])
+
+
 def cpu_baseline(name: str, rows: int = 256):
     import numpy as np
     import oracle
@@ -240,6 +355,10 @@ def main():
                     help="time GROUP_SIZE_M in 1..32 with the XCD permutation on and off (stderr)")
     ap.add_argument("--torch", action="store_true",
                     help="also time torch.matmul on the same operands (stderr, context only)")
+    ap.add_argument("--no-clocks", action="store_true",
+                    help="skip the 3 s clock sampling after the timed region")
+    ap.add_argument("--cpu-all", action="store_true",
+                    help="only time the CPU oracle on every workload (no GPU)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="only time a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -248,6 +367,10 @@ def main():
         print("bench.py measures one GPU only: the GEMM runs on a single MI355X and this build "
               "has no multi-GPU path (run with --gpus 1).", file=sys.stderr)
         sys.exit(2)
+
+    if args.cpu_all:
+        cpu_all()
+        return
 
     import torch
     import dense_gemm_f16f32_amd as g
@@ -296,6 +419,10 @@ def main():
 
     r = time_workload(g, torch, args.workload, args.steps, args.warmup, opts, args.layout)
     plan = r["plan"]
+    clocks = None
+    if not args.no_clocks:
+        Ad, Bd, Cd = layout_views(torch, *device_operands(torch, args.workload), args.layout)
+        clocks = sample_clocks(g, torch, lambda: g.matmul(Ad, Bd, Cd, **opts))
     traffic = (measured_traffic(args.workload, plan["tile"], plan["group_m"], plan["xcd_remap"])
                if args.layout == "nn" else None)
     out = {
@@ -315,8 +442,10 @@ def main():
             "workload": args.workload, "M": r["M"], "N": r["N"], "K": r["K"],
             "accumulate": "f32", "layout": args.layout,
             "path": ["dma", "generic"][plan["path"]],
-            "tile": f"{plan['bm']}x{plan['bn']}x{plan['bk']}", "group_m": plan["group_m"],
+            "tile": f"{plan['bm']}x{plan['bn']}x{plan['bk']}", "tile_id": plan["tile"],
+            "threads": plan["threads"], "group_m": plan["group_m"],
             "xcd_remap": plan["xcd_remap"], "workgroups": plan["num_programs"],
+            "launches": plan["launches"],
         },
         "roofline": {
             "bound": "mfma",
@@ -327,6 +456,14 @@ def main():
             "traffic": traffic,
             "kernel_ms": {k: round(r["kernel_ms_" + k], 5) for k in ("mean", "median", "min",
                                                                       "p90")},
+            # XCD clocks while the same launches run back to back (3 s after the timed region)
+            # and the dense fp16 peak at their median: 256 CUs x 4096 flop/clk x f
+            "sclk_mhz": clocks,
+            "peak_at_sclk": (round(256 * 4096 * clocks["median"] * 1e6 / 1e12, 1)
+                             if clocks else None),
+            "frac_at_sclk": (round(r["achieved_tflops"] /
+                                   (256 * 4096 * clocks["median"] * 1e6 / 1e12), 4)
+                             if clocks else None),
         },
         "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline(args.workload),
     }
