@@ -40,14 +40,24 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = ("gemm_kernels.hpp", "gemm_tiles.hpp")
 
 
+def strip_comments(text: str) -> str:
+    """C++ source without comments and with runs of white space collapsed (the sources have
+    no string literals that contain comment markers)."""
+    import re
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_source_hash() -> str:
-    """sha256 (first 16 hex digits) of the files that fix the kernels' code: the device code
-    and the tile configurations.  The planner and its dispatch table are left out: they choose
-    the launch configuration, which the traffic record's key already names."""
+    """sha256 (first 16 hex digits) of the files that fix the kernels' code -- the device code
+    and the tile configurations -- with comments and white space removed, so that only a code
+    change voids the traffic record.  The planner and its dispatch table are left out: they
+    choose the launch configuration, which the record's key already names."""
     h = hashlib.sha256()
     for name in KERNEL_SOURCES:
-        with open(os.path.join(CSRC, name), "rb") as f:
-            h.update(name.encode() + b"\0" + f.read())
+        with open(os.path.join(CSRC, name)) as f:
+            h.update(name.encode() + b"\0" + strip_comments(f.read()).encode())
     return h.hexdigest()[:16]
 
 

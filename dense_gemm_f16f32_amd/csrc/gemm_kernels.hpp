@@ -2,10 +2,11 @@
 //
 // What is computed: C = A B with fp16 operands, an fp32 accumulator that stays in registers
 // for the whole k loop, and one narrowing to fp16 (round to nearest even) on the store --
-// phobos "03: Matrix multiplication", the `matmul` kernel and the paragraph after it.  One
-// workgroup owns one BM x BN tile of C and walks K in BK = 64 deep panels; each panel of A and
-// of B is staged in LDS and multiplied on the matrix cores; the LDS panels are double
-// buffered so that panel s+1 streams in while panel s is multiplied.
+// phobos "03: Matrix multiplication", the `matmul` kernel and the paragraph after it.  A
+// workgroup of WM x WN wavefronts computes one BM x BN tile of C (or, in the persistent
+// schedule, a sequence of them) and walks K in BK-deep panels; each panel of A and of B is
+// staged in LDS in the operand's own storage order (k-contiguous or not) and multiplied on
+// the matrix cores; NS LDS stages keep the next panels streaming in while one is multiplied.
 //
 // Which tile a workgroup owns follows the grouped order of the kernl notebook "Computing
 // coordinates on Triton GEMM example" (introduction excerpt, cells In[4]-In[7]), applied to a
@@ -17,10 +18,10 @@
 //    B[8(l/32) .. +7][l%32]; result element v of lane l is C[8(v/4) + 4(l/32) + v%4][l%32].
 //  * ds_read_b64_tr_b16: inside each group of 16 lanes, lane i receives, as its 4 halves, the
 //    i-th 16-bit column of the 4 x 16 block whose row e is the 4 x 64 bits addressed by lanes
-//    4e .. 4e+3 of the group.  Row-major B panels therefore yield MFMA B operands (k-runs at a
-//    fixed column) without any transpose in memory.
-//  * global_load_lds_dwordx4: lane l's 16 bytes land at the (wave-uniform) LDS address plus
-//    16 l; the instruction's immediate offset would move both addresses, so it stays 0.
+//    4e .. 4e+3 of the group.  Panels stored with k as the row index therefore yield MFMA
+//    operands (k-runs at a fixed row of A / column of B) without any transpose in memory.
+//  * buffer_load_dwordx4 ... lds: lane l's 16 bytes land at the (wave-uniform) LDS address
+//    plus 16 l; the instruction's immediate offset would move both addresses, so it stays 0.
 #pragma once
 
 #include <hip/hip_runtime.h>

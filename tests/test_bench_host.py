@@ -39,3 +39,10 @@ def test_traffic_is_dropped_when_the_kernel_changes(tmp_path, monkeypatch):
     rec["w/tile1/g8/remap1"]["source_hash"] = bench.kernel_source_hash()
     p.write_text(json.dumps(rec))
     assert bench.measured_traffic("w", 1, 8, 1) == 5
+
+
+def test_source_hash_ignores_comments():
+    code = "int f(int x) {\n  return x + 1;  // one more\n}\n/* block\n comment */\n"
+    assert bench.strip_comments(code) == bench.strip_comments(
+        "int f(int x) { return x + 1; }")
+    assert bench.strip_comments(code) != bench.strip_comments("int f(int x) { return x + 2; }")
