@@ -163,3 +163,16 @@ def test_matmul_reads_transposed_views():
     assert np.array_equal(from_dev(out), ref)
     with pytest.raises(g.GemmError):
         g.matmul(to_dev(A), to_dev(B)[:, ::2], M=M, N=N // 2, K=K)   # no unit stride
+
+
+@pytest.mark.parametrize("M,N", [(4095, 1), (4095, 7), (2000, 31), (1, 3000), (9, 2500), (33, 700)])
+def test_thin_strips_in_every_order(M, N):
+    """Problems narrower than one tile (the shape of split-off edge strips) in every storage
+    order: equal to the row-major result bit for bit, and to the oracle within tolerance."""
+    K = 1021
+    A, B = operands(M, N, K, "n(0,0.1)", M * 3 + N)
+    ref = row_major_result(A, B)
+    assert_within_tolerance(ref, oracle.gemm(A, B), f"{M}x{N}x{K}")
+    for a_col, b_col in [(False, False), (True, False), (False, True), (True, True)]:
+        got = call(place(A, a_col, pad=3), place(B, b_col, pad=3), output(M, N, False))
+        assert np.array_equal(got, ref), (a_col, b_col)
