@@ -22,14 +22,17 @@ OK = 0
 ERR_DIM, ERR_NULL, ERR_LD, ERR_OVERLAP, ERR_OPTS, ERR_TOO_LARGE, ERR_HIP = range(-1, -8, -1)
 (TILE_AUTO, TILE_256x256x64, TILE_128x128x64, TILE_128x64x64, TILE_256x128x64,
  TILE_256x256x32, TILE_64x64x32, TILE_128x64x32, TILE_256x256x64_W8, TILE_64x64x64,
- TILE_32x32x64, TILE_32x64x64, TILE_64x32x64) = range(13)
+ TILE_32x32x64, TILE_32x64x64, TILE_64x32x64, TILE_32x64x128, TILE_64x64x128, TILE_32x32x128,
+ TILE_64x32x128) = range(17)
 # tile id -> (BM, BN, BK, threads)
 TILES = {TILE_256x256x64: (256, 256, 64, 256), TILE_128x128x64: (128, 128, 64, 256),
          TILE_128x64x64: (128, 64, 64, 256), TILE_256x128x64: (256, 128, 64, 256),
          TILE_256x256x32: (256, 256, 32, 256), TILE_64x64x32: (64, 64, 32, 256),
          TILE_128x64x32: (128, 64, 32, 256), TILE_256x256x64_W8: (256, 256, 64, 512),
          TILE_64x64x64: (64, 64, 64, 256), TILE_32x32x64: (32, 32, 64, 64),
-         TILE_32x64x64: (32, 64, 64, 128), TILE_64x32x64: (64, 32, 64, 128)}
+         TILE_32x64x64: (32, 64, 64, 128), TILE_64x32x64: (64, 32, 64, 128),
+         TILE_32x64x128: (32, 64, 128, 128), TILE_64x64x128: (64, 64, 128, 256),
+         TILE_32x32x128: (32, 32, 128, 64), TILE_64x32x128: (64, 32, 128, 128)}
 PATH_DMA, PATH_GENERIC = 0, 1
 REMAP_DEFAULT, REMAP_ON, REMAP_OFF = 0, 1, 2
 SPLIT_DEFAULT, SPLIT_ON, SPLIT_OFF = 0, 1, 2

@@ -103,7 +103,7 @@ struct Opnd {
   static constexpr int NOFF = KM ? BK / 16 : T;      // per-lane LDS read offsets
   static constexpr int READS = KM ? T : 2 * T;       // LDS read instructions per k step
   static_assert(T >= 1 && LD >= 1 && WX % 32 == 0, "operand tile too small for its waves");
-  static_assert(!KM || CH == 8 || CH == 4, "k-major LDS rows hold 64 or 32 halves");
+  static_assert(!KM || CH == 16 || CH == 8 || CH == 4, "k-major LDS rows hold 128-32 halves");
   static_assert(KM || CH == 4 || CH == 8 || CH == 16 || CH == 32,
                 "x-major LDS rows hold 32-256 halves");
 };
@@ -160,6 +160,8 @@ __device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t r, void
 // Swizzles.  The hardware serves a 16-byte-per-lane LDS read 8 lanes (128 B) or 16 lanes
 // (256 B) at a time, so the rows touched by any 8 (and any 16) consecutive lanes must land on
 // distinct bank groups.
+//  * k-major, 256-byte rows (BK = 128): every row starts on the same bank, and swz = r mod 16
+//    puts 16 consecutive rows on the 16 distinct 16-byte bank groups of a 256-byte line.
 //  * k-major, 128-byte rows (BK = 64): 32 lanes read 32 consecutive rows at one logical
 //    chunk; swz = (r mod 8) xor bit 3 of r gives 8 rows 8 distinct chunk positions and 16
 //    rows 16 distinct (row parity, position) pairs.
@@ -175,7 +177,9 @@ __device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t r, void
 template <class O>
 __device__ __forceinline__ int swz(int r) {
   if constexpr (O::KM) {
-    if constexpr (O::CH == 8)
+    if constexpr (O::CH == 16)
+      return r & 15;
+    else if constexpr (O::CH == 8)
       return (r & 7) ^ ((r >> 3) & 1);
     else
       return ((r >> 1) ^ (r >> 3)) & 3;

@@ -20,4 +20,8 @@
   X(GEMM_F16F32_TILE_64x64x64, 64, 64, 64, 4, 3, 2, 2, 4)                \
   X(GEMM_F16F32_TILE_32x32x64, 32, 32, 64, 4, 3, 1, 1, 4)                \
   X(GEMM_F16F32_TILE_32x64x64, 32, 64, 64, 4, 3, 1, 2, 4)                \
-  X(GEMM_F16F32_TILE_64x32x64, 64, 32, 64, 4, 3, 2, 1, 4)
+  X(GEMM_F16F32_TILE_64x32x64, 64, 32, 64, 4, 3, 2, 1, 4)                \
+  X(GEMM_F16F32_TILE_32x64x128, 32, 64, 128, 4, 3, 1, 2, 4)              \
+  X(GEMM_F16F32_TILE_64x64x128, 64, 64, 128, 3, 3, 2, 2, 4)              \
+  X(GEMM_F16F32_TILE_32x32x128, 32, 32, 128, 4, 3, 1, 1, 4)              \
+  X(GEMM_F16F32_TILE_64x32x128, 64, 32, 128, 4, 3, 2, 1, 4)

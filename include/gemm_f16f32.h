@@ -80,7 +80,11 @@ enum {
     GEMM_F16F32_TILE_64x64x64 = 9,       /* 4 stages, read 3 ahead */
     GEMM_F16F32_TILE_32x32x64 = 10,      /* 1 wavefront, 4 stages, read 3 ahead */
     GEMM_F16F32_TILE_32x64x64 = 11,      /* 2 wavefronts (1 x 2), 4 stages, read 3 ahead */
-    GEMM_F16F32_TILE_64x32x64 = 12       /* 2 wavefronts (2 x 1), 4 stages, read 3 ahead */
+    GEMM_F16F32_TILE_64x32x64 = 12,      /* 2 wavefronts (2 x 1), 4 stages, read 3 ahead */
+    GEMM_F16F32_TILE_32x64x128 = 13,     /* 2 wavefronts (1 x 2), 4 stages, read 3 ahead */
+    GEMM_F16F32_TILE_64x64x128 = 14,     /* 3 stages, read 3 ahead */
+    GEMM_F16F32_TILE_32x32x128 = 15,     /* 1 wavefront, 4 stages, read 3 ahead */
+    GEMM_F16F32_TILE_64x32x128 = 16      /* 2 wavefronts (2 x 1), 4 stages, read 3 ahead */
 };
 
 /* Kernel families.  Both accept any shape, leading dimension and 2-byte alignment. */
