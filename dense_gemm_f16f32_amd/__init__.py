@@ -1,11 +1,12 @@
 """Python binding of libgemm_f16f32.so (the gfx950 fp16/fp32-accumulate GEMM).
 
 The functions named like the C-ABI (gemm_f16f32, gemm_f16f32_ex, gemm_f16f32_plan,
-gemm_f16f32_strided, gemm_f16f32_strided_plan, gemm_f16f32_tile_map, gemm_f16f32_strerror,
-gemm_f16f32_version) only marshal arguments into the library; every step of the computation
-runs in its HIP kernels.  `matmul` is the same call for torch tensors: it passes their device
-pointers, element strides (row- or column-major, any leading dimension) and torch's current
-HIP stream.  PyTorch is used for device memory and streams only.
+gemm_f16f32_strided, gemm_f16f32_strided_ws, gemm_f16f32_strided_plan, gemm_f16f32_tile_map,
+gemm_f16f32_strerror, gemm_f16f32_version) only marshal arguments into the library; every step
+of the computation runs in its HIP kernels.  `matmul` is the same call for torch tensors: it
+passes their device pointers, element strides (row- or column-major, any leading dimension)
+and torch's current HIP stream, and for split K a workspace tensor.  PyTorch is used for
+device memory and streams only.
 
 The library is loaded on first use; if it has not been built the call raises at once
 (there is no fallback of any kind).
@@ -19,7 +20,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libgemm_f16f32.so")
 
 OK = 0
-ERR_DIM, ERR_NULL, ERR_LD, ERR_OVERLAP, ERR_OPTS, ERR_TOO_LARGE, ERR_HIP = range(-1, -8, -1)
+(ERR_DIM, ERR_NULL, ERR_LD, ERR_OVERLAP, ERR_OPTS, ERR_TOO_LARGE, ERR_HIP,
+ ERR_WORKSPACE) = range(-1, -9, -1)
 (TILE_AUTO, TILE_256x256x64, TILE_128x128x64, TILE_128x64x64, TILE_256x128x64,
  TILE_256x256x32, TILE_64x64x32, TILE_128x64x32, TILE_256x256x64_W8, TILE_64x64x64,
  TILE_32x32x64, TILE_32x64x64, TILE_64x32x64, TILE_32x64x128, TILE_64x64x128, TILE_32x32x128,
@@ -37,6 +39,7 @@ PATH_DMA, PATH_GENERIC = 0, 1
 REMAP_DEFAULT, REMAP_ON, REMAP_OFF = 0, 1, 2
 SPLIT_DEFAULT, SPLIT_ON, SPLIT_OFF = 0, 1, 2
 PERSISTENT_DEFAULT, PERSISTENT_ON, PERSISTENT_OFF = 0, 1, 2
+SPLIT_K_AUTO = -1
 
 
 class GemmError(RuntimeError):
@@ -48,7 +51,8 @@ class GemmError(RuntimeError):
 class Opts(ctypes.Structure):
     _fields_ = [("tile", ctypes.c_int32), ("group_m", ctypes.c_int32),
                 ("xcd_remap", ctypes.c_int32), ("force_generic", ctypes.c_int32),
-                ("split_edges", ctypes.c_int32), ("persistent", ctypes.c_int32)]
+                ("split_edges", ctypes.c_int32), ("persistent", ctypes.c_int32),
+                ("split_k", ctypes.c_int32)]
 
 
 class PlanInfo(ctypes.Structure):
@@ -56,7 +60,8 @@ class PlanInfo(ctypes.Structure):
                                               "xcd_remap", "num_pid_m", "num_pid_n",
                                               "num_programs", "launches", "main_m", "main_n",
                                               "a_kmajor", "b_kmajor", "swapped", "threads",
-                                              "persistent", "grid")]
+                                              "persistent", "grid", "splits", "split_depth")
+               ] + [("workspace_bytes", ctypes.c_int64)]
 
     def as_dict(self) -> dict:
         return {n: getattr(self, n) for n, _ in self._fields_}
@@ -86,6 +91,9 @@ def lib() -> ctypes.CDLL:
         L.gemm_f16f32_plan.restype = ctypes.c_int
         L.gemm_f16f32_strided.argtypes = _STRIDED_ARGS + [_vp, ctypes.POINTER(Opts)]
         L.gemm_f16f32_strided.restype = ctypes.c_int
+        L.gemm_f16f32_strided_ws.argtypes = _STRIDED_ARGS + [_vp, _i64, _vp,
+                                                             ctypes.POINTER(Opts)]
+        L.gemm_f16f32_strided_ws.restype = ctypes.c_int
         L.gemm_f16f32_strided_plan.argtypes = _STRIDED_ARGS + [ctypes.POINTER(Opts),
                                                                ctypes.POINTER(PlanInfo)]
         L.gemm_f16f32_strided_plan.restype = ctypes.c_int
@@ -134,6 +142,16 @@ def gemm_f16f32_strided(M, N, K, A, stride_am, stride_ak, B, stride_bk, stride_b
                                      ctypes.byref(o) if o is not None else None)
 
 
+def gemm_f16f32_strided_ws(M, N, K, A, stride_am, stride_ak, B, stride_bk, stride_bn, C,
+                           stride_cm, stride_cn, workspace, workspace_bytes, stream=None,
+                           opts=None) -> int:
+    o = _opts(opts)
+    return lib().gemm_f16f32_strided_ws(M, N, K, A, stride_am, stride_ak, B, stride_bk,
+                                        stride_bn, C, stride_cm, stride_cn, workspace,
+                                        workspace_bytes, stream,
+                                        ctypes.byref(o) if o is not None else None)
+
+
 def gemm_f16f32_strided_plan(M, N, K, A, stride_am, stride_ak, B, stride_bk, stride_bn, C,
                              stride_cm, stride_cn, opts=None):
     """(code, dict of the plan) -- host only, nothing is launched."""
@@ -166,14 +184,17 @@ def _stream_handle(stream):
     return s.cuda_stream
 
 
-def matmul(a, b, out=None, *, M=None, N=None, K=None, stream=None, **opts):
+def matmul(a, b, out=None, *, M=None, N=None, K=None, stream=None, workspace=None, **opts):
     """out[:M, :N] = fp16(a[:M, :K] @ b[:K, :N]) on the GPU (fp32 accumulation).
 
     a, b, out: 2-D CUDA tensors of 16-bit elements (float16, or int16 holding fp16 bits),
     each row-major or column-major (one unit stride) with any leading dimension: transposed
     views such as `w.t()` are read in place.  opts: tile, group_m, xcd_remap, force_generic,
-    split_edges (see include/gemm_f16f32.h).  Raises GemmError on a non-zero return code.
-    Launches on torch's current stream unless `stream` is given.
+    split_edges, persistent, split_k (see include/gemm_f16f32.h).  Split K goes through
+    gemm_f16f32_strided_ws: with split_k >= 2 or SPLIT_K_AUTO, and also whenever a
+    `workspace` (a CUDA tensor) is given, split_k then defaulting to SPLIT_K_AUTO.  A needed
+    workspace that is not given is allocated by torch for this call.  Raises GemmError on a
+    non-zero return code.  Launches on torch's current stream unless `stream` is given.
     """
     import torch
     M = a.shape[0] if M is None else M
@@ -186,12 +207,28 @@ def matmul(a, b, out=None, *, M=None, N=None, K=None, stream=None, **opts):
             raise ValueError("expected 2-D tensors")
         if t.element_size() != 2 or not t.is_cuda:
             raise ValueError("operands must be 16-bit CUDA tensors")
-    rc = gemm_f16f32_strided(M, N, K, a.data_ptr(), a.stride(0), a.stride(1), b.data_ptr(),
-                             b.stride(0), b.stride(1), out.data_ptr(), out.stride(0),
-                             out.stride(1), _stream_handle(stream),
-                             Opts(**opts) if opts else None)
+    args = (M, N, K, a.data_ptr(), a.stride(0), a.stride(1), b.data_ptr(), b.stride(0),
+            b.stride(1), out.data_ptr(), out.stride(0), out.stride(1))
+    if workspace is not None and "split_k" not in opts:
+        opts = dict(opts, split_k=SPLIT_K_AUTO)
+    o = Opts(**opts) if opts else None
+    if o is None or o.split_k in (0, 1):
+        rc = gemm_f16f32_strided(*args, _stream_handle(stream), o)
+        if rc != OK:
+            raise GemmError(rc, "gemm_f16f32_strided")
+        return out
+    if workspace is None:
+        rc, info = gemm_f16f32_strided_plan(*args, opts=o)
+        if rc != OK:
+            raise GemmError(rc, "gemm_f16f32_strided_plan")
+        if info["workspace_bytes"] > 0:
+            workspace = torch.empty(info["workspace_bytes"], dtype=torch.uint8,
+                                    device=out.device)
+    ptr, nbytes = (0, 0) if workspace is None else (workspace.data_ptr(),
+                                                    workspace.numel() * workspace.element_size())
+    rc = gemm_f16f32_strided_ws(*args, ptr, nbytes, _stream_handle(stream), o)
     if rc != OK:
-        raise GemmError(rc, "gemm_f16f32_strided")
+        raise GemmError(rc, "gemm_f16f32_strided_ws")
     return out
 
 

@@ -12,7 +12,7 @@
 
 namespace {
 
-constexpr int kVersion = 300;  // 0.3.0
+constexpr int kVersion = 400;  // 0.4.0
 constexpr int kCUs = 256;       // compute units of an MI355X (the persistent grid's width)
 
 struct TileDesc {
@@ -137,6 +137,26 @@ int order_of(int64_t R, int64_t S, int64_t sr, int64_t sc, int64_t* ld) {
   return -1;
 }
 
+// 16-byte aligned rows of both operands (the dispatch table's measurement condition).
+bool aligned_rows(const Problem& pr) {
+  return (((uintptr_t)pr.A | (uintptr_t)pr.B) & 15) == 0 && pr.lda % 8 == 0 && pr.ldb % 8 == 0;
+}
+
+// Slices of the automatic split K.  A slice computes M x N x L on its own workgroups, so a
+// split pays when the unsplit grid leaves most CUs idle and K is deep: one workgroup streams
+// its panels through one CU at that CU's fetch rate, S slices through S CUs.  Measured on
+// MI355X (graph-timed, M, N in 32 .. 4096, K in 1024 .. 8192): the best S kept the grid
+// within the 256 CUs and every slice at least 512 deep; two slices paid off only from
+// K = 4096 on (the reduction's launch and fp32 traffic cost about 1-2 us).  So: the largest
+// power of two S <= 16 with S * programs <= 256 and K >= 512 S, and S = 2 only for K >= 4096.
+int auto_splits(int64_t M, int64_t N, int64_t K, int tile, bool aligned) {
+  const TileDesc* t = find_tile(tile ? tile : choose_tile(M, N, K, aligned).tile);
+  const int64_t P = cdiv(M, t->bm) * cdiv(N, t->bn);
+  int S = 1;
+  while (S < 16 && P * S * 2 <= kCUs && K >= 512 * (int64_t)S * 2) S *= 2;
+  return (S == 2 && K < 4096) ? 1 : S;
+}
+
 // One launch over an M x N block of C (all of it, or one part of an edge split).
 struct Part {
   int64_t m_off, n_off, M, N;
@@ -184,6 +204,30 @@ int plan_launch(const Problem& pr, int64_t M, int64_t N, const TileDesc* t, int 
   r->a_kmajor = pr.a_kmajor;
   r->b_kmajor = pr.b_kmajor;
   r->swapped = pr.swapped;
+  r->splits = 1;
+  r->split_depth = 0;
+  r->workspace_bytes = 0;
+  return GEMM_F16F32_OK;
+}
+
+// Split K over the whole M x N launch: slices of L = roundup(cdiv(K, S), 128) k values cut
+// from the end of k (the first slice holds the rest), S' = cdiv(K, L) <= S of them.  Writes
+// splits, split_depth, workspace_bytes (S' slices of M x ldw fp32, ldw = N rounded up to a
+// multiple of 4), grid = S' P and launches = 2 (the slices, then the reduction).
+int plan_split(const Problem& pr, int64_t L, gemm_f16f32_plan_info* r) {
+  const int64_t kMax = (int64_t)1 << 31;
+  const int64_t S = cdiv(pr.K, L);
+  const int64_t ldw = cdiv(pr.N, 4) * 4;
+  // 32-bit workspace offsets within one tile's rows; the x extent of the slice grid; the
+  // reduction's 32-bit thread index (one thread per 4 workspace elements of a slice)
+  if ((int64_t)r->bm * ldw * 4 >= kMax || S * r->num_programs >= kMax ||
+      pr.M * (ldw / 4) >= kMax)
+    return GEMM_F16F32_ERR_TOO_LARGE;
+  r->splits = (int32_t)S;
+  r->split_depth = (int32_t)L;
+  r->workspace_bytes = S * pr.M * ldw * 4;
+  r->grid = (int32_t)(S * r->num_programs);
+  r->launches = 2;
   return GEMM_F16F32_OK;
 }
 
@@ -197,7 +241,11 @@ int plan_launch(const Problem& pr, int64_t M, int64_t N, const TileDesc* t, int 
 // sliver is then computed by separate launches with tiles chosen for its own shape.  Every
 // element's k-sum is the same sequence of MFMA steps whatever the tile, so results do not
 // change.
-int plan_parts(const Problem& pr, const gemm_f16f32_opts* opts, Part* parts, int* nparts) {
+//
+// ws_bytes: the caller's split-K workspace (-1: the entry point takes none).  The automatic
+// split (split_k = -1) is planned only when a workspace is given and used only when it fits.
+int plan_parts(const Problem& pr, const gemm_f16f32_opts* opts, int64_t ws_bytes, Part* parts,
+               int* nparts) {
   const int64_t kMax = (int64_t)1 << 31;
   const int64_t M = pr.M, N = pr.N, K = pr.K;
   *nparts = 0;
@@ -211,13 +259,29 @@ int plan_parts(const Problem& pr, const gemm_f16f32_opts* opts, Part* parts, int
   if (!emptyC && K > 0 && (pr.A == nullptr || pr.B == nullptr)) return GEMM_F16F32_ERR_NULL;
   if (((uintptr_t)pr.A | (uintptr_t)pr.B | (uintptr_t)pr.C) & 1) return GEMM_F16F32_ERR_OPTS;
 
-  gemm_f16f32_opts o = {0, 0, 0, 0, 0, 0};
+  gemm_f16f32_opts o = {0, 0, 0, 0, 0, 0, 0};
   if (opts) o = *opts;
   if (o.tile != 0 && find_tile(o.tile) == nullptr) return GEMM_F16F32_ERR_OPTS;
   if (o.group_m < 0 || o.xcd_remap < 0 || o.xcd_remap > 2 || o.force_generic < 0 ||
       o.force_generic > 1 || o.split_edges < 0 || o.split_edges > 2 || o.persistent < 0 ||
-      o.persistent > 2)
+      o.persistent > 2 || o.split_k < GEMM_F16F32_SPLIT_K_AUTO)
     return GEMM_F16F32_ERR_OPTS;
+  if (o.split_k == GEMM_F16F32_SPLIT_K_AUTO) {
+    const bool may = ws_bytes > 0 && !emptyC && o.force_generic != 1 && o.persistent != 1;
+    const int S = may ? auto_splits(M, N, K, o.tile, aligned_rows(pr)) : 1;
+    if (S > 1) {
+      gemm_f16f32_opts os = o;
+      os.split_k = S;
+      const int rc = plan_parts(pr, &os, ws_bytes, parts, nparts);
+      if (rc == GEMM_F16F32_OK && parts[0].r.workspace_bytes <= ws_bytes) return rc;
+    }
+    o.split_k = 1;   // no split: not worth it, no workspace, or it does not fit
+  }
+  // Split K: asked for with split_k >= 2; it takes effect when K spans more than one slice.
+  if (o.split_k >= 2 && (o.force_generic == 1 || o.persistent == 1))
+    return GEMM_F16F32_ERR_OPTS;
+  const int64_t L = o.split_k >= 2 ? cdiv(cdiv(K, o.split_k), 128) * 128 : 0;
+  const bool split_k = L > 0 && K > L && !emptyC;
 
   if (!emptyC) {
     const uint64_t fc = footprint(M, N, pr.ldc);
@@ -227,13 +291,13 @@ int plan_parts(const Problem& pr, const gemm_f16f32_opts* opts, Part* parts, int
       return GEMM_F16F32_ERR_OVERLAP;
   }
 
-  // 16-byte aligned rows of both operands (the table's measurement condition)
-  const bool aligned = (((uintptr_t)pr.A | (uintptr_t)pr.B) & 15) == 0 && pr.lda % 8 == 0 &&
-                       pr.ldb % 8 == 0;
-  const Choice ch = o.tile ? Choice{o.tile, 0} : choose_tile(M, N, K, aligned);
+  const bool aligned = aligned_rows(pr);
+  // A split problem is chosen for as the slices' own shape, M x N x L.
+  const Choice ch = o.tile ? Choice{o.tile, 0} : choose_tile(M, N, split_k ? L : K, aligned);
   const TileDesc* t = find_tile(ch.tile);
   int64_t Mm = M, Nm = N;
-  const bool split = o.split_edges == 1 || (o.split_edges == 0 && o.tile == 0);
+  const bool split =
+      !split_k && (o.split_edges == 1 || (o.split_edges == 0 && o.tile == 0));
   if (split && !emptyC) {
     const int64_t rm = M % t->bm, rn = N % t->bn;
     const int64_t full_m = M / t->bm, full_n = N / t->bn;
@@ -246,6 +310,10 @@ int plan_parts(const Problem& pr, const gemm_f16f32_opts* opts, Part* parts, int
   pp->m_off = 0, pp->n_off = 0, pp->M = Mm, pp->N = Nm;
   int rc = plan_launch(pr, Mm, Nm, t, ch.group, o, &pp->r);
   if (rc != GEMM_F16F32_OK) return rc;
+  if (split_k) {
+    *nparts = 1;
+    return plan_split(pr, L, &parts[0].r);
+  }
   ++pp;
   const int64_t strips[3][4] = {{0, Nm, Mm, N - Nm}, {Mm, 0, M - Mm, Nm}, {Mm, Nm, M - Mm, N - Nm}};
   gemm_f16f32_opts os = o;
@@ -268,7 +336,10 @@ template <int BM, int BN, int BK, int NS, int RD, int WM, int WN, bool AKM, bool
 hipError_t launch_layout(const gemm_f16f32_plan_info& r, const gk::Args& a, bool odd,
                          hipStream_t stream) {
   const dim3 grid(r.grid), block(64 * WM * WN);
-  if (r.path == GEMM_F16F32_PATH_DMA && r.persistent)
+  if (r.splits > 1)
+    hipLaunchKernelGGL((gk::gemm_dma_splitk<BM, BN, BK, NS, RD, WM, WN, AKM, BKM>), grid, block,
+                       0, stream, a);
+  else if (r.path == GEMM_F16F32_PATH_DMA && r.persistent)
     hipLaunchKernelGGL((gk::gemm_dma_persistent<BM, BN, BK, NS, RD, WM, WN, AKM, BKM>), grid,
                        block, 0, stream, a);
   else if (r.path == GEMM_F16F32_PATH_DMA)
@@ -297,7 +368,8 @@ hipError_t launch(const gemm_f16f32_plan_info& r, const gk::Args& a, bool odd,
              : launch_layout<BM, BN, BK, NS, RD, WM, WN, false, false>(r, a, odd, stream);
 }
 
-int launch_part(const Problem& pr, const Part& pt, hipStream_t s) {
+// Launches one part; `ws` is the split-K workspace (used only when r.splits > 1).
+int launch_part(const Problem& pr, const Part& pt, float* ws, hipStream_t s) {
   const gemm_f16f32_plan_info& r = pt.r;
   if (r.num_programs == 0) return GEMM_F16F32_OK;
   gk::Args a;
@@ -315,6 +387,10 @@ int launch_part(const Problem& pr, const Part& pt, hipStream_t s) {
   a.group_m = r.group_m;
   a.xcd_remap = r.xcd_remap;
   a.num_programs = r.num_programs;
+  a.W = ws;
+  a.ldw = cdiv(pt.N, 4) * 4;
+  a.splits = r.splits;
+  a.panels_per_split = r.splits > 1 ? r.split_depth / r.bk : 0;
   const bool odd = (((uintptr_t)a.A | (uintptr_t)a.B) & 3) != 0 || ((pr.lda | pr.ldb) & 1) != 0;
   hipError_t e = hipSuccess;
   switch (r.tile) {
@@ -323,6 +399,12 @@ int launch_part(const Problem& pr, const Part& pt, hipStream_t s) {
     GEMM_F16F32_TILES(GEMM_F16F32_TILE_CASE)
 #undef GEMM_F16F32_TILE_CASE
     default: return GEMM_F16F32_ERR_OPTS;
+  }
+  if (e == hipSuccess && r.splits > 1) {
+    const int64_t threads = pt.M * (a.ldw / 4);
+    hipLaunchKernelGGL(gk::splitk_reduce, dim3((uint32_t)cdiv(threads, 256)), dim3(256), 0, s,
+                       (const float*)ws, a.ldw, (int)r.splits, a.M, a.N, a.C, a.ldc);
+    e = hipGetLastError();
   }
   return e == hipSuccess ? GEMM_F16F32_OK : GEMM_F16F32_ERR_HIP;
 }
@@ -352,19 +434,35 @@ int strided_problem(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t 
   return GEMM_F16F32_OK;
 }
 
-int run(const Problem& pr, void* stream, const gemm_f16f32_opts* opts) {
+// Plans, checks the workspace against the plan (ws_bytes < 0: the entry point has none),
+// then launches every part.
+int run(const Problem& pr, void* stream, const gemm_f16f32_opts* opts, void* ws,
+        int64_t ws_bytes) {
   Part parts[4];
   int n = 0;
-  int rc = plan_parts(pr, opts, parts, &n);
+  int rc = plan_parts(pr, opts, ws_bytes, parts, &n);
+  if (rc != GEMM_F16F32_OK) return rc;
+  const gemm_f16f32_plan_info& r = parts[0].r;
+  if (n > 0 && r.splits > 1) {
+    if (ws == nullptr || ws_bytes < r.workspace_bytes || ((uintptr_t)ws & 15) != 0)
+      return GEMM_F16F32_ERR_WORKSPACE;
+    const uint64_t fw = (uint64_t)r.workspace_bytes;
+    const uint64_t fc = footprint(pr.M, pr.N, pr.ldc);
+    const uint64_t fa = pr.a_kmajor ? footprint(pr.M, pr.K, pr.lda) : footprint(pr.K, pr.M, pr.lda);
+    const uint64_t fb = pr.b_kmajor ? footprint(pr.N, pr.K, pr.ldb) : footprint(pr.K, pr.N, pr.ldb);
+    if (overlaps(ws, fw, pr.C, fc) || overlaps(ws, fw, pr.A, fa) || overlaps(ws, fw, pr.B, fb))
+      return GEMM_F16F32_ERR_OVERLAP;
+  }
   for (int i = 0; i < n && rc == GEMM_F16F32_OK; ++i)
-    rc = launch_part(pr, parts[i], (hipStream_t)stream);
+    rc = launch_part(pr, parts[i], (float*)ws, (hipStream_t)stream);
   return rc;
 }
 
 int plan(const Problem& pr, const gemm_f16f32_opts* opts, gemm_f16f32_plan_info* info) {
   Part parts[4];
   int n = 0;
-  const int rc = plan_parts(pr, opts, parts, &n);
+  // the plan reports the automatic split as if a large enough workspace were given
+  const int rc = plan_parts(pr, opts, INT64_MAX, parts, &n);
   if (rc == GEMM_F16F32_OK && info) *info = parts[0].r;
   return rc;
 }
@@ -382,7 +480,7 @@ int gemm_f16f32_plan(int64_t M, int64_t N, int64_t K, const uint16_t* A, const u
 int gemm_f16f32_ex(int64_t M, int64_t N, int64_t K, const uint16_t* A, const uint16_t* B,
                    uint16_t* C, int64_t lda, int64_t ldb, int64_t ldc, void* stream,
                    const gemm_f16f32_opts* opts) {
-  return run(row_major_problem(M, N, K, A, B, C, lda, ldb, ldc), stream, opts);
+  return run(row_major_problem(M, N, K, A, B, C, lda, ldb, ldc), stream, opts, nullptr, -1);
 }
 
 int gemm_f16f32(int64_t M, int64_t N, int64_t K, const uint16_t* A, const uint16_t* B,
@@ -397,7 +495,18 @@ int gemm_f16f32_strided(int64_t M, int64_t N, int64_t K, const uint16_t* A, int6
   Problem pr;
   const int rc = strided_problem(M, N, K, A, stride_am, stride_ak, B, stride_bk, stride_bn, C,
                                  stride_cm, stride_cn, &pr);
-  return rc != GEMM_F16F32_OK ? rc : run(pr, stream, opts);
+  return rc != GEMM_F16F32_OK ? rc : run(pr, stream, opts, nullptr, -1);
+}
+
+int gemm_f16f32_strided_ws(int64_t M, int64_t N, int64_t K, const uint16_t* A,
+                           int64_t stride_am, int64_t stride_ak, const uint16_t* B,
+                           int64_t stride_bk, int64_t stride_bn, uint16_t* C, int64_t stride_cm,
+                           int64_t stride_cn, void* workspace, int64_t workspace_bytes,
+                           void* stream, const gemm_f16f32_opts* opts) {
+  Problem pr;
+  const int rc = strided_problem(M, N, K, A, stride_am, stride_ak, B, stride_bk, stride_bn, C,
+                                 stride_cm, stride_cn, &pr);
+  return rc != GEMM_F16F32_OK ? rc : run(pr, stream, opts, workspace, workspace_bytes);
 }
 
 int gemm_f16f32_strided_plan(int64_t M, int64_t N, int64_t K, const uint16_t* A,
@@ -433,6 +542,8 @@ const char* gemm_f16f32_strerror(int code) {
     case GEMM_F16F32_ERR_OPTS: return "invalid option or misaligned pointer";
     case GEMM_F16F32_ERR_TOO_LARGE: return "leading dimension too large for 32-bit tile offsets";
     case GEMM_F16F32_ERR_HIP: return "HIP runtime rejected the launch";
+    case GEMM_F16F32_ERR_WORKSPACE:
+      return "split K needs a 16-byte aligned workspace of at least plan_info.workspace_bytes";
     default: return "unknown error code";
   }
 }

@@ -35,6 +35,7 @@ namespace gk {
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef short short4v __attribute__((ext_vector_type(4)));
 typedef float float16v __attribute__((ext_vector_type(16)));
+typedef float float4v __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 #define GK_LDS __attribute__((address_space(3)))
 
@@ -49,6 +50,11 @@ struct Args {
   int64_t lda, ldb, ldc;
   int32_t M, N, K;
   int32_t num_pid_m, num_pid_n, group_m, xcd_remap, num_programs;
+  // Split K only (gemm_dma_splitk): slice z of every tile sums its k panels into the fp32
+  // workspace W[z][i][j] at W + (z M + i) ldw + j instead of narrowing into C.
+  float* W;
+  int64_t ldw;
+  int32_t splits, panels_per_split;
 };
 
 // ---------------------------------------------------------------------------------------
@@ -333,6 +339,39 @@ __device__ __forceinline__ void store_tile(const Args& p, const float16v (&acc)[
     block(std::false_type{});
 }
 
+// Split-K epilogue: the fp32 accumulators of one k slice, unrounded, into the workspace (same
+// lane layout and masks as store_tile; the slice's M x N block starts at `w`).
+template <class T>
+__device__ __forceinline__ void store_partial(const Args& p, float* w,
+                                             const float16v (&acc)[T::TM][T::TN], int m0,
+                                             int n0, int wm, int wn, int lane) {
+  const int64_t w0 = (int64_t)m0 * p.ldw + n0;
+  const int64_t extW = (int64_t)(p.M - 1) * p.ldw + p.N;
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(w + w0, 4 * (extW - w0));
+  const int col = wn * T::WTN + (lane & 31);
+  const int row = wm * T::WTM + (lane >> 5) * 4;
+  const uint32_t vbase = 4u * ((uint32_t)row * (uint32_t)p.ldw + (uint32_t)col);
+  const uint32_t ldw4 = 4u * (uint32_t)p.ldw;
+  const int ncols = p.N - n0, nrows = p.M - m0;
+#pragma unroll
+  for (int tn = 0; tn < T::TN; ++tn) {
+    if (col + tn * 32 < ncols) {
+#pragma unroll
+      for (int tm = 0; tm < T::TM; ++tm) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int r = tm * 32 + (v >> 2) * 8 + (v & 3);
+          // the element by value first: a bit_cast of the subscript itself reads element 0
+          const float x = acc[tm][tn][v];
+          if (row + r < nrows)
+            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, x), rw,
+                                                  vbase + tn * 128, (uint32_t)r * ldw4, 0);
+        }
+      }
+    }
+  }
+}
+
 // Wait for this wave's LDS accesses, then meet the other waves.  Written as one asm block so
 // that no LDS access is moved across it.
 __device__ __forceinline__ void lds_barrier() {
@@ -517,11 +556,14 @@ __device__ __forceinline__ int last_element_slot(int x0, int X, int K, const uin
       (char GK_LDS*)stage12, (char GK_LDS*)stage13, (char GK_LDS*)stage14,                    \
       (char GK_LDS*)stage15};
 
-// One BM x BN tile of C with corner (m0, n0): the whole k loop and the store, on the LDS
-// stages S.
-template <int BM, int BN, int BK, int NS, int RD, int WM, int WN, bool AKM, bool BKM>
+// One BM x BN tile of C with corner (m0, n0) on the LDS stages S: the k loop over all panels
+// and the store narrowed into C, or (SPLIT) over panels [p0, p1) with the fp32 partial stored
+// into the workspace block `ws`.
+template <int BM, int BN, int BK, int NS, int RD, int WM, int WN, bool AKM, bool BKM,
+          bool SPLIT = false>
 __device__ __forceinline__ void dma_tile(const Args& p, int m0, int n0,
-                                         char GK_LDS* const (&S)[kMaxStages]) {
+                                         char GK_LDS* const (&S)[kMaxStages], int p0 = 0,
+                                         int p1 = 0, float* ws = nullptr) {
   using T = Tile<BM, BN, BK, AKM, BKM, WM, WN>;
   using OA = typename T::OA;
   using OB = typename T::OB;
@@ -549,9 +591,16 @@ __device__ __forceinline__ void dma_tile(const Args& p, int m0, int n0,
 
   const int64_t extA = extent<AKM>(p.M, p.K, p.lda);
   const int64_t extB = extent<BKM>(p.N, p.K, p.ldb);
-  const int rk = p.K % BK;                       // depth of the head panel (0: none)
-  const int np = p.K / BK + (rk ? 1 : 0);        // panels
-  const int kofs = rk ? rk - BK : 0;             // panel s covers k in [kofs + s BK, + BK)
+  const int rk0 = p.K % BK;                      // depth of the head panel (0: none)
+  const int np_all = p.K / BK + (rk0 ? 1 : 0);   // panels of the whole k range
+  // Split K: this call's panels are [p0, p1) of the whole sequence (0 < p0 < p1 <= np_all or
+  // p0 == 0), renumbered from 0.  Only the slice holding panel 0 has the head; only the one
+  // holding the last panel patches.
+  const int np = SPLIT ? p1 - p0 : np_all;       // panels of this call
+  const int rk = SPLIT && p0 != 0 ? 0 : rk0;
+  const bool has_last = !SPLIT || p1 == np_all;
+  // panel s covers k in [kofs + s BK, + BK)
+  const int kofs = (rk0 ? rk0 - BK : 0) + (SPLIT ? p0 * BK : 0);
 
   uint16_t last_a = 0, last_b = 0;
   const int patch_a = last_element_slot<OA>(m0, p.M, p.K, p.A, extA, tid, last_a);
@@ -608,7 +657,7 @@ __device__ __forceinline__ void dma_tile(const Args& p, int m0, int n0,
       }
       if (kk == KS - RD) {
         wait_vmcnt<(NS - 2) * NV>();   // panel s+1 has landed (this wave's part)
-        if (s + 2 == np) patch(nxt);   // panel s+1 is the last one
+        if (has_last && s + 2 == np) patch(nxt);   // panel s+1 is the last one
         lds_barrier();                 // ... every wave's part
         if constexpr (NS == 2) issue(s + NS, cur);
       }
@@ -637,7 +686,7 @@ __device__ __forceinline__ void dma_tile(const Args& p, int m0, int n0,
 #pragma unroll
     for (int j = 1; j < kPre; ++j) issue(j, S[j]);
     wait_vmcnt<(kPre - 1) * NV>();
-    if (np == 1) patch(S[0]);
+    if (has_last && np == 1) patch(S[0]);
     lds_barrier();
 #pragma unroll
     for (int d = 0; d < RD; ++d) read_frags<T>(f[d], S[0], lo, d);
@@ -650,7 +699,10 @@ __device__ __forceinline__ void dma_tile(const Args& p, int m0, int n0,
   // The last refills (of panels past the end) must land before the workgroup's LDS is freed
   // (or reused for another tile).
   wait_vmcnt<0>();
-  store_tile<T>(p, acc, m0, n0, wm, wn, lane);
+  if constexpr (SPLIT)
+    store_partial<T>(p, ws, acc, m0, n0, wm, wn, lane);
+  else
+    store_tile<T>(p, acc, m0, n0, wm, wn, lane);
 }
 
 // One workgroup per program: hardware id -> program id -> tile.
@@ -679,6 +731,60 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_dma_persistent(Args p) {
                  pid_m, pid_n);
     dma_tile<BM, BN, BK, NS, RD, WM, WN, AKM, BKM>(p, pid_m * BM, pid_n * BN, S);
     __syncthreads();   // every wave is done with the stages before the next tile's prologue
+  }
+}
+
+// Split K: the k range is cut into `splits` slices at k = K - L, K - 2L, ... (L a multiple of
+// 128 k values, so every tile's panel boundaries fall on the cuts and the slices' sums do not
+// depend on the tile): slice z < splits - 1 ends panels_per_split = L / BK panels before the
+// next, and slice 0 holds what is left in front, head panel included.  Workgroup
+// b = z P + h (P programs) computes slice z of the tile of program h, h going through the same
+// map as a hardware id of the one-workgroup-per-program launch; the fp32 partial goes to
+// W[z].  `splitk_reduce` then adds the slices in order and narrows once.
+template <int BM, int BN, int BK, int NS, int RD, int WM, int WN, bool AKM, bool BKM>
+__global__ void __launch_bounds__(64 * WM * WN) gemm_dma_splitk(Args p) {
+  GK_DECLARE_STAGES(NS, (Tile<BM, BN, BK, AKM, BKM, WM, WN>::STAGE))
+  const int z = blockIdx.x / p.num_programs;
+  const int h = blockIdx.x - z * p.num_programs;
+  int pid, pid_m, pid_n;
+  program_tile(h, p.num_programs, p.num_pid_m, p.num_pid_n, p.group_m, p.xcd_remap, pid, pid_m,
+               pid_n);
+  const int np_all = p.K / BK + (p.K % BK ? 1 : 0);
+  const int p1 = np_all - (p.splits - 1 - z) * p.panels_per_split;
+  const int p0 = z == 0 ? 0 : p1 - p.panels_per_split;
+  dma_tile<BM, BN, BK, NS, RD, WM, WN, AKM, BKM, true>(
+      p, pid_m * BM, pid_n * BN, S, p0, p1, p.W + (int64_t)z * p.M * p.ldw);
+}
+
+// C[i][j] = fp16(W[0][i][j] + W[1][i][j] + ... + W[splits-1][i][j]): the slices added in
+// order in fp32, then one narrowing (round to nearest even).  Thread t covers row
+// i = t / (ldw / 4), columns j .. j + 3 with j = 4 (t mod (ldw / 4)); ldw is a multiple of 4
+// and W 16-byte aligned, so the reads are whole float4s (columns past N are read, not stored).
+__global__ void __launch_bounds__(256) splitk_reduce(const float* W, int64_t ldw, int splits,
+                                                     int M, int N, uint16_t* C, int64_t ldc) {
+  const uint32_t q4 = (uint32_t)(ldw >> 2);   // M q4 < 2^31 (checked on the host)
+  const uint32_t t = blockIdx.x * 256u + threadIdx.x;
+  if (t >= (uint32_t)M * q4) return;
+  const uint32_t i = t / q4;
+  const int j = (int)(t - i * q4) * 4;
+  const int64_t slice = (int64_t)M * ldw;
+  const float* w = W + (int64_t)i * ldw + j;
+  // loads issued 8 at a time (in flight together), added strictly in slice order
+  float4v sum = *(const float4v*)w;
+  int z = 1;
+  for (; z + 8 <= splits; z += 8) {
+    float4v v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = *(const float4v*)(w + (z + u) * slice);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) sum += v[u];
+  }
+  for (; z < splits; ++z) sum += *(const float4v*)(w + z * slice);
+  uint16_t* c = C + (int64_t)i * ldc + j;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const _Float16 h = (_Float16)sum[e];
+    if (j + e < N) c[e] = __builtin_bit_cast(uint16_t, h);
   }
 }
 

@@ -26,9 +26,9 @@
  * column-major storage, any leading dimension).  Values are IEEE binary16 bit patterns passed
  * as uint16_t.
  *
- * Ownership and execution: A, B, C are device pointers owned by the caller.  The library
- * allocates nothing and keeps no state between calls, so calls from several host threads are
- * safe.  A call checks its arguments, launches on `stream` (a hipStream_t; NULL is the null
+ * Ownership and execution: A, B, C (and the split-K workspace of gemm_f16f32_strided_ws) are
+ * device pointers owned by the caller.  The library allocates nothing and keeps no state
+ * between calls, so calls from several host threads are safe.  A call checks its arguments, launches on `stream` (a hipStream_t; NULL is the null
  * stream) and returns without waiting; faults inside a kernel surface at the caller's next
  * synchronisation.  Only C[i][j] with i < M, j < N is written (padding between N and ldc is
  * left as it was).  M == 0 or N == 0 is a successful no-op; K == 0 writes +0 to the M x N
@@ -58,8 +58,13 @@ enum {
     GEMM_F16F32_ERR_TOO_LARGE = -6, /* a leading dimension beyond the kernels' 32-bit offsets:
                                        BM * ldc, and for each operand (rows of one stored
                                        panel) * ld must stay below 2^31, where a panel has BM
-                                       (BN) rows when k is the unit-stride axis, else 64 */
-    GEMM_F16F32_ERR_HIP = -7        /* the HIP runtime rejected the launch */
+                                       (BN) rows when k is the unit-stride axis, else 64; with
+                                       split K also BM * ldw * 4 bytes, M * ldw / 4 and the
+                                       grid splits * programs (ldw = N rounded up to 4) */
+    GEMM_F16F32_ERR_HIP = -7,       /* the HIP runtime rejected the launch */
+    GEMM_F16F32_ERR_WORKSPACE = -8  /* split K planned but no workspace (an entry point without
+                                       one), or the workspace is smaller than
+                                       plan_info.workspace_bytes or not 16-byte aligned */
 };
 
 /* Tile configurations: BM x BN x BK, computed by a workgroup of wavefronts (64 lanes each)
@@ -87,6 +92,9 @@ enum {
     GEMM_F16F32_TILE_64x32x128 = 16      /* 2 wavefronts (2 x 1), 4 stages, read 3 ahead */
 };
 
+/* opts.split_k: the library chooses the number of k slices (see gemm_f16f32_opts). */
+#define GEMM_F16F32_SPLIT_K_AUTO (-1)
+
 /* Kernel families.  Both accept any shape, leading dimension and 2-byte alignment. */
 enum {
     GEMM_F16F32_PATH_DMA = 0,     /* default: 16-byte buffer->LDS loads of full BK-deep
@@ -111,6 +119,20 @@ typedef struct gemm_f16f32_opts {
                               launches one round of workgroups (256 CUs x as many per CU as fit
                               in LDS, a multiple of 8) and workgroup h computes programs h,
                               h + grid, ... through the same map; results are unchanged. 2 = off */
+    int32_t split_k;       /* 0 or 1 = no split (default).  S >= 2: split K into at most S slices
+                              of L = roundup(cdiv(K, S), 128) k values, cut from the end of k
+                              (the first slice holds the rest), when K > L.  Each slice's fp32
+                              tile sums go to a caller workspace (gemm_f16f32_strided_ws), a
+                              second kernel adds the slices in order in fp32 and narrows once.
+                              Results then depend on L (not on the tile) and stay within the
+                              tolerance of the unsplit sum.  The tile is chosen for M x N x L;
+                              no edge split; not with force_generic or persistent = 1 (ERR_OPTS).
+                              Helps when M x N has too few tiles to fill the chip and K is deep.
+                              GEMM_F16F32_SPLIT_K_AUTO (-1): the library picks S from the shape
+                              (S = 1 when a split would not pay); only gemm_f16f32_strided_ws
+                              acts on it, and only when its workspace holds the plan's
+                              workspace_bytes (otherwise, and for the other entry points, the
+                              call runs unsplit).  Plans report the automatic choice. */
 } gemm_f16f32_opts;
 
 /* What a call with these arguments would launch (filled by gemm_f16f32_plan).  The fields
@@ -136,7 +158,14 @@ typedef struct gemm_f16f32_plan_info {
                               N, bn, num_pid_n, main_n along M */
     int32_t threads;       /* workgroup size of the main launch */
     int32_t persistent;    /* 1 if the main launch uses the persistent schedule */
-    int32_t grid;          /* workgroups of the main launch (num_programs unless persistent) */
+    int32_t grid;          /* workgroups of the main launch (num_programs unless persistent;
+                              splits * num_programs when split) */
+    int32_t splits;        /* k slices (1 = no split K) */
+    int32_t split_depth;   /* k values per slice L (0 = no split K) */
+    int64_t workspace_bytes; /* workspace the call needs, splits * M' * roundup(N', 4) * 4 bytes
+                              where M' x N' is the launch's C (M x N, or N x M when swapped):
+                              slice z's fp32 sums at workspace + 4 (z M' + i) roundup(N', 4) + 4 j;
+                              0 without split K */
 } gemm_f16f32_plan_info;
 
 /*
@@ -177,7 +206,25 @@ int gemm_f16f32_strided(int64_t M, int64_t N, int64_t K, const uint16_t *A, int6
                         int64_t stride_bn, uint16_t *C, int64_t stride_cm, int64_t stride_cn,
                         void *stream, const gemm_f16f32_opts *opts);
 
-/* Host only, no GPU work: what gemm_f16f32_strided with these arguments would launch. */
+/*
+ * gemm_f16f32_strided with a caller-owned device workspace for split K (opts->split_k >= 2):
+ * workspace must be 16-byte aligned, hold at least the plan's workspace_bytes, and overlap
+ * none of A, B, C (ERR_WORKSPACE, ERR_OVERLAP otherwise).  The call launches the slice
+ * kernel and the reduction on `stream`, one after the other; the workspace is scratch that is
+ * read and written by those two kernels only and may be reused once they are done (stream
+ * order), so calls in flight at the same time need separate workspaces.  Without a split
+ * (split_k 0 or 1, or K no deeper than one slice) the workspace is not touched and the call is
+ * gemm_f16f32_strided.  The other entry points return ERR_WORKSPACE when split_k asks for a
+ * split that would take place.
+ */
+int gemm_f16f32_strided_ws(int64_t M, int64_t N, int64_t K, const uint16_t *A,
+                           int64_t stride_am, int64_t stride_ak, const uint16_t *B,
+                           int64_t stride_bk, int64_t stride_bn, uint16_t *C, int64_t stride_cm,
+                           int64_t stride_cn, void *workspace, int64_t workspace_bytes,
+                           void *stream, const gemm_f16f32_opts *opts);
+
+/* Host only, no GPU work: what gemm_f16f32_strided (or, with split_k, gemm_f16f32_strided_ws)
+ * with these arguments would launch, including the workspace a split needs. */
 int gemm_f16f32_strided_plan(int64_t M, int64_t N, int64_t K, const uint16_t *A,
                              int64_t stride_am, int64_t stride_ak, const uint16_t *B,
                              int64_t stride_bk, int64_t stride_bn, const uint16_t *C,

@@ -15,43 +15,15 @@ import pytest
 
 import dense_gemm_f16f32_amd as g
 import oracle
-from gpu_util import assert_within_tolerance, from_dev, to_dev
+from gpu_util import (assert_within_tolerance, from_dev, output, padding_untouched, place,
+                      to_dev)
 from synthetic_inputs import operands
 
 pytestmark = pytest.mark.gpu
 
 torch = pytest.importorskip("torch")
 
-NAN = 0x7E00
-CANARY = 0x5A5A
 LAYOUTS = list(itertools.product((False, True), repeat=3))  # (A col-major, B col-major, C col-major)
-
-
-def place(X, col_major, pad=0, offset=0, fill=NAN):
-    """Device copy of the logical R x S matrix X (fp16 bits) stored row- or column-major with
-    `pad` extra elements per stored row and its first element `offset` elements into the
-    buffer.  Returns the logical (R, S) view (a transposed view when column-major)."""
-    stored = np.ascontiguousarray(X.T if col_major else X)
-    rows, cols = stored.shape
-    ld = cols + pad
-    buf = torch.full((offset + rows * ld + 8,), fill, dtype=torch.int16, device="cuda")
-    body = buf[offset:offset + rows * ld].view(rows, ld)
-    body[:, :cols] = to_dev(stored)
-    view = body[:, :cols]
-    return view.t() if col_major else view
-
-
-def output(M, N, col_major, pad=3):
-    return place(np.zeros((M, N), np.uint16), col_major, pad, fill=CANARY)
-
-
-def padding_untouched(C_view, col_major):
-    """The ld padding of C's storage still holds the canary."""
-    stored = C_view.t() if col_major else C_view
-    rows, cols = stored.shape
-    ld = stored.stride(0)
-    flat = torch.as_strided(stored, (rows, ld), (ld, 1))
-    return bool((flat[:, cols:] == CANARY).all())
 
 
 def call(Av, Bv, Cv, **opts):

@@ -12,7 +12,8 @@ import pytest
 
 import dense_gemm_f16f32_amd as g
 import oracle
-from gpu_util import assert_within_tolerance, f64, from_dev, to_dev
+from gpu_util import (assert_within_tolerance, checksum_ok, f64, from_dev, sample_positions,
+                      to_dev)
 from synthetic_inputs import operands, workload
 
 pytestmark = pytest.mark.gpu
@@ -79,39 +80,6 @@ def test_workload_1024x768x128_grouped_full():
 # ---------------------------------------------------------------------------------------
 # Full-size workloads: sampled elements and checksums.
 # ---------------------------------------------------------------------------------------
-def sample_positions(M, N, bm, bn, per_tile, seed):
-    """Per output tile: its four corners plus `per_tile` random elements; plus C's corners."""
-    rng = np.random.default_rng(seed)
-    rows, cols = [], []
-    for tm in range(0, M, bm):
-        for tn in range(0, N, bn):
-            r1, c1 = min(tm + bm, M) - 1, min(tn + bn, N) - 1
-            rows += [tm, tm, r1, r1]
-            cols += [tn, c1, tn, c1]
-            rows += list(rng.integers(tm, r1 + 1, per_tile))
-            cols += list(rng.integers(tn, c1 + 1, per_tile))
-    rows += [0, 0, M - 1, M - 1]
-    cols += [0, N - 1, 0, N - 1]
-    return np.array(rows, dtype=np.int64), np.array(cols, dtype=np.int64)
-
-
-def checksum_ok(A, B, C):
-    """Row and column sums of C against A (B 1) and (1^T A) B in fp64.
-
-    Each C element is within 1e-2 + 2^-10 |C| of the exact sum, so a row's total error is
-    within N * 1e-2 + 2^-10 sum|C| (and likewise per column); a wrong or missing tile, a
-    dropped k panel or a misplaced row breaks these by far more.
-    """
-    a, b, c = f64(A), f64(B), f64(C)
-    row_want = a @ b.sum(axis=1)
-    col_want = a.sum(axis=0) @ b
-    row_err = np.abs(c.sum(axis=1) - row_want)
-    col_err = np.abs(c.sum(axis=0) - col_want)
-    row_bound = c.shape[1] * 1e-2 + 2.0 ** -10 * np.abs(c).sum(axis=1)
-    col_bound = c.shape[0] * 1e-2 + 2.0 ** -10 * np.abs(c).sum(axis=0)
-    return bool(np.all(row_err <= row_bound) and np.all(col_err <= col_bound))
-
-
 @pytest.mark.parametrize("name", ["gemm4096_u", "gemm8192_u", "gemm4095x4097x4093_n"])
 def test_large_workload_sampled(name):
     _, M, N, K, dist, seed = workload(name)
