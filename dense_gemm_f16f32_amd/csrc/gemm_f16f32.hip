@@ -145,16 +145,19 @@ bool aligned_rows(const Problem& pr) {
 // Slices of the automatic split K.  A slice computes M x N x L on its own workgroups, so a
 // split pays when the unsplit grid leaves most CUs idle and K is deep: one workgroup streams
 // its panels through one CU at that CU's fetch rate, S slices through S CUs.  Measured on
-// MI355X (graph-timed, M, N in 32 .. 4096, K in 1024 .. 8192): the best S kept the grid
-// within the 256 CUs and every slice at least 512 deep; two slices paid off only from
-// K = 4096 on (the reduction's launch and fp32 traffic cost about 1-2 us).  So: the largest
-// power of two S <= 16 with S * programs <= 256 and K >= 512 S, and S = 2 only for K >= 4096.
+// MI355X (graph-timed, M, N in 32 .. 4096, K in 1024 .. 8192): the best S kept the split grid
+// (S times the programs of the tile chosen for M x N x L) within the 256 CUs and every slice
+// at least 512 deep; two slices paid off only from K = 4096 on (the reduction's launch and
+// fp32 traffic cost about 1-2 us).  So: the largest power of two S <= 16 with that grid
+// within 256 and K >= 512 S, and S = 2 only for K >= 4096.
 int auto_splits(int64_t M, int64_t N, int64_t K, int tile, bool aligned) {
-  const TileDesc* t = find_tile(tile ? tile : choose_tile(M, N, K, aligned).tile);
-  const int64_t P = cdiv(M, t->bm) * cdiv(N, t->bn);
-  int S = 1;
-  while (S < 16 && P * S * 2 <= kCUs && K >= 512 * (int64_t)S * 2) S *= 2;
-  return (S == 2 && K < 4096) ? 1 : S;
+  int best = 1;
+  for (int S = 2; S <= 16 && K >= 512 * (int64_t)S; S *= 2) {
+    const int64_t L = cdiv(cdiv(K, S), 128) * 128;
+    const TileDesc* t = find_tile(tile ? tile : choose_tile(M, N, L, aligned).tile);
+    if (cdiv(M, t->bm) * cdiv(N, t->bn) * S <= kCUs) best = S;
+  }
+  return (best == 2 && K < 4096) ? 1 : best;
 }
 
 // One launch over an M x N block of C (all of it, or one part of an edge split).

@@ -18,6 +18,11 @@ median.  Every forced configuration must also reproduce the first
 configuration's bits (all tiles add the same MFMA k steps per element).
 
     python -m dense_gemm_f16f32_amd.tune [--out PATH] [--quick]
+
+`--split-sweep` instead times split K (gemm_f16f32_strided_ws with split_k = S, the tile
+chosen by the planner for each slice shape) for S in 1, 2, 4, ..., 32 and the automatic
+choice, on thin and deep shapes, and prints one JSON line per shape: the data behind the
+planner's automatic split rule.
 """
 from __future__ import annotations
 
@@ -153,6 +158,38 @@ def tune_shape(torch, M, N, K, quick=False):
             "auto_us": round(auto, 2)}
 
 
+SPLIT_SHAPES = [(32, 32), (64, 64), (128, 128), (256, 256), (512, 512), (1024, 1024),
+                (2048, 2048), (64, 4096), (4096, 64), (256, 2048), (128, 8192), (4095, 1)]
+SPLIT_K = [1024, 2048, 4096, 8192]
+SPLITS = [1, 2, 4, 8, 16, 32]
+
+
+def split_sweep(torch):
+    """Device time per call (us) of each split count and of the automatic choice."""
+    ws = torch.empty(600 << 20, dtype=torch.uint8, device="cuda")
+    for M, N in SPLIT_SHAPES:
+        for K in SPLIT_K:
+            gen = torch.Generator(device="cuda")
+            gen.manual_seed(M * 1000003 + N * 1009 + K)
+            A = (torch.rand((M, K), device="cuda", generator=gen) - 0.5).half()
+            B = (torch.rand((K, N), device="cuda", generator=gen) - 0.5).half()
+            C = torch.empty((M, N), dtype=torch.half, device="cuda")
+            row = {"M": M, "N": N, "K": K}
+            for S in SPLITS + [g.SPLIT_K_AUTO]:
+                rc, info = g.gemm_f16f32_strided_plan(M, N, K, A.data_ptr(), K, 1, B.data_ptr(),
+                                                      N, 1, C.data_ptr(), N, 1,
+                                                      opts=dict(split_k=S))
+                if rc != g.OK:
+                    raise RuntimeError(g.gemm_f16f32_strerror(rc))
+                if S > 1 and info["splits"] < 2:
+                    continue
+                us = graph_time_us(torch, lambda: g.matmul(A, B, C, workspace=ws, split_k=S))
+                key = "auto" if S == g.SPLIT_K_AUTO else str(S)
+                row[key] = {"us": round(us, 2), "tile": info["tile"],
+                            "splits": info["splits"], "grid": info["grid"]}
+            print(json.dumps(row), flush=True)
+
+
 def write_table(path, results, device):
     lines = [
         "// Tile configuration and GROUP_SIZE_M per shape class, written by",
@@ -183,7 +220,14 @@ def main():
     ap.add_argument("--quick", action="store_true", help="skip grids above 4096 workgroups")
     ap.add_argument("--from-json", default=None,
                     help="only rewrite the table from a JSON file of an earlier sweep")
+    ap.add_argument("--split-sweep", action="store_true",
+                    help="time split K per split count instead (no table is written)")
     args = ap.parse_args()
+    if args.split_sweep:
+        import torch
+        torch.cuda.set_device(0)
+        split_sweep(torch)
+        return
     if args.from_json:
         with open(args.from_json) as f:
             rec = json.load(f)

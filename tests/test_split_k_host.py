@@ -135,14 +135,16 @@ def test_strerror_names_the_workspace():
 
 
 def auto_rule(M, N, K):
-    """The documented automatic choice: the largest power of two S <= 16 with
-    S * programs <= 256 and K >= 512 S (programs of the unsplit tile), S = 2 only from
-    K = 4096 on."""
-    P = plan(M, N, K, split_edges=g.SPLIT_OFF)["num_programs"]
-    S = 1
-    while S < 16 and P * S * 2 <= 256 and K >= 512 * S * 2:
+    """The documented automatic choice: the largest power of two S <= 16 with K >= 512 S whose
+    split grid (S times the programs of the tile planned for M x N x L) fits in 256 CUs;
+    S = 2 only from K = 4096 on."""
+    best, S = 1, 2
+    while S <= 16 and K >= 512 * S:
+        L = cdiv(cdiv(K, S), 128) * 128
+        if plan(M, N, L, split_edges=g.SPLIT_OFF)["num_programs"] * S <= 256:
+            best = S
         S *= 2
-    return 1 if (S == 2 and K < 4096) else S
+    return 1 if (best == 2 and K < 4096) else best
 
 
 @pytest.mark.parametrize("M,N,K", [(32, 32, 8192), (32, 32, 1024), (64, 64, 2048),
