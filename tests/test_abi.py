@@ -326,3 +326,31 @@ def test_misaligned_rows_take_the_eight_wavefront_tile():
     assert plan(M, N, K, a=PA + 2)["tile"] == g.TILE_256x256x64_W8
     assert plan(M, N, K, lda=K + 8)["tile"] == g.TILE_256x256x64
     assert plan(4095, 4097, 4093)["tile"] == g.TILE_256x256x64_W8
+
+
+def test_struct_layouts_match_the_header(tmp_path):
+    """Every field of gemm_f16f32_opts and gemm_f16f32_plan_info sits at the same offset (and
+    each struct has the same size) in the C header, compiled by gcc, as in the ctypes binding."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("gcc not available")
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "gemm_f16f32.h"',
+             'int main(void) {']
+    for cname, py in (("gemm_f16f32_opts", g.Opts), ("gemm_f16f32_plan_info", g.PlanInfo)):
+        lines.append(f'  printf("{cname} size %zu\\n", sizeof({cname}));')
+        for field, _ in py._fields_:
+            lines.append(f'  printf("{cname} {field} %zu\\n", offsetof({cname}, {field}));')
+    lines += ['  return 0;', '}']
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines) + "\n")
+    exe = tmp_path / "layout"
+    subprocess.run([gcc, "-std=c99", "-Wall", "-Werror", "-I", os.path.join(ROOT, "include"),
+                    str(src), "-o", str(exe)], check=True)
+    out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split("\n")
+    got = {tuple(ln.split()[:2]): int(ln.split()[2]) for ln in out if ln}
+    for cname, py in (("gemm_f16f32_opts", g.Opts), ("gemm_f16f32_plan_info", g.PlanInfo)):
+        assert got[(cname, "size")] == ctypes.sizeof(py), cname
+        for field, _ in py._fields_:
+            assert got[(cname, field)] == getattr(py, field).offset, (cname, field)
