@@ -8,6 +8,10 @@
 // staged in LDS in the operand's own storage order (k-contiguous or not) and multiplied on
 // the matrix cores; NS LDS stages keep the next panels streaming in while one is multiplied.
 //
+// Split K (opt-in, with a caller workspace): the k range is cut into slices whose partial
+// tile sums are stored in fp32 and added in slice order by a second kernel before the one
+// narrowing -- still one fp32 sum per element, rounded once, in another order of additions.
+//
 // Which tile a workgroup owns follows the grouped order of the kernl notebook "Computing
 // coordinates on Triton GEMM example" (introduction excerpt, cells In[4]-In[7]), applied to a
 // program id that is first permuted so that the workgroups one XCD receives (the hardware
