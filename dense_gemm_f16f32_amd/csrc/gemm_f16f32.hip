@@ -13,7 +13,7 @@
 namespace {
 
 constexpr int kVersion = 400;  // 0.4.0
-constexpr int kCUs = 256;       // compute units of an MI355X (the persistent grid's width)
+constexpr int kCUs = 256;       // compute units of an MI355X (persistent grid width, split-K grid budget)
 
 struct TileDesc {
   int id, bm, bn, bk, stages, read_ahead, wm, wn, default_group;
