@@ -22,7 +22,7 @@ configuration's bits (all tiles add the same MFMA k steps per element).
 `--split-sweep` instead times split K (gemm_f16f32_strided_ws with split_k = S, the tile
 chosen by the planner for each slice shape) for S in 1, 2, 4, ..., 32 and the automatic
 choice, on thin and deep shapes, and prints one JSON line per shape: the data behind the
-planner's automatic split rule.
+planner's automatic split rule (`--shapes` and `--splits` narrow it).
 """
 from __future__ import annotations
 
@@ -164,30 +164,33 @@ SPLIT_K = [1024, 2048, 4096, 8192]
 SPLITS = [1, 2, 4, 8, 16, 32]
 
 
-def split_sweep(torch):
-    """Device time per call (us) of each split count and of the automatic choice."""
+def split_sweep(torch, shapes=None, splits=None):
+    """Device time per call (us) of each split count and of the automatic choice, over the
+    grid SPLIT_SHAPES x SPLIT_K or the given (M, N, K) list; `splits` restricts the split
+    counts (SPLIT_K_AUTO for the automatic choice)."""
     ws = torch.empty(600 << 20, dtype=torch.uint8, device="cuda")
-    for M, N in SPLIT_SHAPES:
-        for K in SPLIT_K:
-            gen = torch.Generator(device="cuda")
-            gen.manual_seed(M * 1000003 + N * 1009 + K)
-            A = (torch.rand((M, K), device="cuda", generator=gen) - 0.5).half()
-            B = (torch.rand((K, N), device="cuda", generator=gen) - 0.5).half()
-            C = torch.empty((M, N), dtype=torch.half, device="cuda")
-            row = {"M": M, "N": N, "K": K}
-            for S in SPLITS + [g.SPLIT_K_AUTO]:
-                rc, info = g.gemm_f16f32_strided_plan(M, N, K, A.data_ptr(), K, 1, B.data_ptr(),
-                                                      N, 1, C.data_ptr(), N, 1,
-                                                      opts=dict(split_k=S))
-                if rc != g.OK:
-                    raise RuntimeError(g.gemm_f16f32_strerror(rc))
-                if S > 1 and info["splits"] < 2:
-                    continue
-                us = graph_time_us(torch, lambda: g.matmul(A, B, C, workspace=ws, split_k=S))
-                key = "auto" if S == g.SPLIT_K_AUTO else str(S)
-                row[key] = {"us": round(us, 2), "tile": info["tile"],
-                            "splits": info["splits"], "grid": info["grid"]}
-            print(json.dumps(row), flush=True)
+    if shapes is None:
+        shapes = [(M, N, K) for M, N in SPLIT_SHAPES for K in SPLIT_K]
+    for M, N, K in shapes:
+        gen = torch.Generator(device="cuda")
+        gen.manual_seed(M * 1000003 + N * 1009 + K)
+        A = (torch.rand((M, K), device="cuda", generator=gen) - 0.5).half()
+        B = (torch.rand((K, N), device="cuda", generator=gen) - 0.5).half()
+        C = torch.empty((M, N), dtype=torch.half, device="cuda")
+        row = {"M": M, "N": N, "K": K}
+        for S in (splits or SPLITS + [g.SPLIT_K_AUTO]):
+            rc, info = g.gemm_f16f32_strided_plan(M, N, K, A.data_ptr(), K, 1, B.data_ptr(),
+                                                  N, 1, C.data_ptr(), N, 1,
+                                                  opts=dict(split_k=S))
+            if rc != g.OK:
+                raise RuntimeError(g.gemm_f16f32_strerror(rc))
+            if S > 1 and info["splits"] < 2:
+                continue
+            us = graph_time_us(torch, lambda: g.matmul(A, B, C, workspace=ws, split_k=S))
+            key = "auto" if S == g.SPLIT_K_AUTO else str(S)
+            row[key] = {"us": round(us, 2), "tile": info["tile"],
+                        "splits": info["splits"], "grid": info["grid"]}
+        print(json.dumps(row), flush=True)
 
 
 def write_table(path, results, device):
@@ -222,11 +225,22 @@ def main():
                     help="only rewrite the table from a JSON file of an earlier sweep")
     ap.add_argument("--split-sweep", action="store_true",
                     help="time split K per split count instead (no table is written)")
+    ap.add_argument("--shapes", default=None,
+                    help="with --split-sweep: comma-separated MxNxK list instead of the grid")
+    ap.add_argument("--splits", default=None,
+                    help="with --split-sweep: comma-separated split counts, 'auto' for the "
+                         "automatic choice (default: 1, 2, 4, 8, 16, 32, auto)")
     args = ap.parse_args()
     if args.split_sweep:
         import torch
         torch.cuda.set_device(0)
-        split_sweep(torch)
+        shapes = None
+        if args.shapes:
+            shapes = [tuple(int(x) for x in sh.split("x")) for sh in args.shapes.split(",")]
+        splits = None
+        if args.splits:
+            splits = [g.SPLIT_K_AUTO if x == "auto" else int(x) for x in args.splits.split(",")]
+        split_sweep(torch, shapes, splits)
         return
     if args.from_json:
         with open(args.from_json) as f:
