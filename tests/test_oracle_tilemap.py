@@ -62,14 +62,16 @@ def test_pointer_printout_differences():
 
 
 def test_bijection_by_enumeration():
-    for m in range(1, 25):
-        for n in range(1, 25):
-            for G in list(range(1, 12)) + [m, m + 1, 40]:
+    """Every pid in [0, P) gets a distinct tile, for all num_pid_m, num_pid_n <= 40 and
+    GROUP_SIZE_M <= 41 (G past num_pid_m included)."""
+    for m in range(1, 41):
+        for n in range(1, 41):
+            for G in range(1, 42):
                 t = oracle.tile_map_all(m, n, G)
                 assert t[:, 0].min() >= 0 and t[:, 0].max() < m
                 assert t[:, 1].min() >= 0 and t[:, 1].max() < n
                 code = t[:, 0] * n + t[:, 1]
-                assert np.unique(code).size == m * n, (m, n, G)
+                assert np.bincount(code, minlength=m * n).max() == 1, (m, n, G)
 
 
 @pytest.mark.parametrize("m,n", [(1, 1), (3, 7), (8, 12), (16, 17), (13, 5)])
