@@ -80,16 +80,24 @@ Choice choose_tile(int64_t M, int64_t N, int64_t K, bool aligned) {
 }
 
 // Bytes from a matrix's first element to one past its last, for rows x cols at leading
-// dimension ld (0 if empty).
+// dimension ld (0 if empty); saturates at UINT64_MAX (rows, cols < 2^31 here, ld any value
+// the caller passed, so the product is taken in 128 bits).
 uint64_t footprint(int64_t rows, int64_t cols, int64_t ld) {
   if (rows <= 0 || cols <= 0) return 0;
-  return 2ull * (uint64_t)((rows - 1) * ld + cols);
+  const __int128 b = 2 * ((__int128)(rows - 1) * ld + cols);
+  return b > (__int128)UINT64_MAX ? UINT64_MAX : (uint64_t)b;
 }
 
+// Whether [a, a + na) and [b, b + nb) intersect, without forming either end address.
 bool overlaps(const void* a, uint64_t na, const void* b, uint64_t nb) {
   if (na == 0 || nb == 0) return false;
   const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
-  return x < y + nb && y < x + na;
+  return x >= y ? x - y < nb : y - x < na;
+}
+
+// rows * ld >= limit, for rows, limit > 0 and any ld >= 0, without overflow.
+bool product_reaches(int64_t rows, int64_t ld, int64_t limit) {
+  return (__int128)rows * ld >= limit;
 }
 
 // A problem as the kernels see it: C (M x N, row-major, ldc) = A (M x K) B (K x N), each
@@ -173,7 +181,8 @@ int plan_launch(const Problem& pr, int64_t M, int64_t N, const TileDesc* t, int 
   // 32-bit in-kernel offsets: one panel's stored rows of A (bm rows if k-major, else up to 64
   // k rows) and of B (bn or 64), and one tile's bm rows of C.
   const int64_t rows_a = pr.a_kmajor ? t->bm : gk::kBK, rows_b = pr.b_kmajor ? t->bn : gk::kBK;
-  if (rows_a * pr.lda >= kMax || rows_b * pr.ldb >= kMax || (int64_t)t->bm * pr.ldc >= kMax)
+  if (product_reaches(rows_a, pr.lda, kMax) || product_reaches(rows_b, pr.ldb, kMax) ||
+      product_reaches(t->bm, pr.ldc, kMax))
     return GEMM_F16F32_ERR_TOO_LARGE;
   const bool dma = !o.force_generic;
   r->path = dma ? GEMM_F16F32_PATH_DMA : GEMM_F16F32_PATH_GENERIC;
