@@ -253,7 +253,7 @@ def sample_clocks(g, torch, fn, seconds=3.0):
     t_end = time.perf_counter() + seconds
     th.start()
     prev = None
-    while time.perf_counter() < t_end:
+    while True:
         for _ in range(20):
             fn()
         ev = torch.cuda.Event()
@@ -261,7 +261,10 @@ def sample_clocks(g, torch, fn, seconds=3.0):
         if prev is not None:     # one batch stays queued, so the GPU never idles
             prev.synchronize()
         prev = ev
-    done.set()
+        if time.perf_counter() >= t_end:
+            done.set()           # the poller may be inside a sample: keep the GPU busy
+            if not th.is_alive():  # until it has returned, so no sample sees it idle
+                break
     th.join()
     torch.cuda.synchronize()
     if not samples:
