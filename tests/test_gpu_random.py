@@ -24,7 +24,7 @@ pytestmark = pytest.mark.gpu
 
 torch = pytest.importorskip("torch")
 
-CASES = 80
+CASES = 200
 
 
 def log_uniform(rng, lo, hi):
