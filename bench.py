@@ -377,7 +377,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: the GEMM runs on a single MI355X and this build "
+        print("bench.py measures one GPU only: the GEMM runs on a single MI355X and the library "
               "has no multi-GPU path (run with --gpus 1).", file=sys.stderr)
         sys.exit(2)
 
