@@ -740,11 +740,11 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_dma_persistent(Args p) {
 
 // Split K: the k range is cut into `splits` slices at k = K - L, K - 2L, ... (L a multiple of
 // 128 k values, so every tile's panel boundaries fall on the cuts and the slices' sums do not
-// depend on the tile): slice z < splits - 1 ends panels_per_split = L / BK panels before the
-// next, and slice 0 holds what is left in front, head panel included.  Workgroup
-// b = z P + h (P programs) computes slice z of the tile of program h, h going through the same
-// map as a hardware id of the one-workgroup-per-program launch; the fp32 partial goes to
-// W[z].  `splitk_reduce` then adds the slices in order and narrows once.
+// depend on the tile): slices 1 .. splits-1 hold panels_per_split = L / BK panels each,
+// counted back from the last panel, and slice 0 holds the panels in front of them, head panel
+// included.  Workgroup b = z P + h (P programs) computes slice z of the tile of program h, h
+// going through the same map as a hardware id of the one-workgroup-per-program launch; the
+// fp32 partial goes to W[z].  `splitk_reduce` then adds the slices in order and narrows once.
 template <int BM, int BN, int BK, int NS, int RD, int WM, int WN, bool AKM, bool BKM>
 __global__ void __launch_bounds__(64 * WM * WN) gemm_dma_splitk(Args p) {
   GK_DECLARE_STAGES(NS, (Tile<BM, BN, BK, AKM, BKM, WM, WN>::STAGE))
