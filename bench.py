@@ -235,7 +235,8 @@ def gfx_clocks_mhz():
 
 def sample_clocks(g, torch, fn, seconds=3.0):
     """Runs fn back to back for `seconds` (untimed, after the timed region) while sampling the
-    XCD clocks; returns min / median / max MHz over all samples and XCDs, or None."""
+    XCD clocks; returns the 5th percentile, median and 95th percentile in MHz over all samples
+    and XCDs, or None."""
     import threading
     samples, done = [], threading.Event()
 
@@ -250,9 +251,12 @@ def sample_clocks(g, torch, fn, seconds=3.0):
         fn()
     torch.cuda.synchronize()
     th = threading.Thread(target=poll, daemon=True)
+    for _ in range(20):          # work is queued before the first sample is taken
+        fn()
+    prev = torch.cuda.Event()
+    prev.record()
     t_end = time.perf_counter() + seconds
     th.start()
-    prev = None
     while True:
         for _ in range(20):
             fn()
