@@ -7,7 +7,7 @@ HIP events recorded on the stream the kernel is launched on (torch's current str
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--all]
                     [--tile T] [--group-m G] [--xcd-remap R] [--layout AB[C]]
-                    [--layouts] [--no-cpu-baseline]
+                    [--layouts] [--dist D] [--no-cpu-baseline]
 
 `value` is TFLOP/s = 2 M N K K_steps / (timed wall time); `roofline.achieved` is
 2 M N K / (mean per-launch event time), against the MI355X published dense fp16 matrix
@@ -16,7 +16,10 @@ rounding) on one 256-row band of the same product, using all host threads it get
 --all prints one extra JSON line per workload to stderr, with the device time per launch
 from HIP-graph replays beside the per-launch event times.  --layout stores A, B (and C) row-
 major ("n") or column-major ("t"), e.g. "nt" for B given as an N x K matrix; --layouts times
-all eight storage orders (stderr).
+all eight storage orders (stderr).  --dist draws the operands from another distribution of
+synthetic_inputs (e.g. "zeros" or "s(1/64)", which switch fewer bits in the matrix cores)
+with the workload's shape and seed; `config.dist` names the one used.  After the timed region
+the same launches run for 3 s while the XCD clocks and the socket power are sampled.
 """
 from __future__ import annotations
 
@@ -79,19 +82,21 @@ def measured_traffic(workload: str, tile: int, group_m: int, remap: int):
 _DEVICE_OPERANDS = {}
 
 
-def device_operands(torch, name):
-    """(A, B, C) device tensors of a workload, generated once per process."""
+def device_operands(torch, name, dist=None):
+    """(A, B, C) device tensors of a workload (operands from `dist` instead of the workload's
+    own distribution if given), generated once per process."""
     import numpy as np
     from synthetic_inputs import operands, workload
 
-    if name not in _DEVICE_OPERANDS:
+    key = (name, dist)
+    if key not in _DEVICE_OPERANDS:
         _DEVICE_OPERANDS.clear()
-        _, M, N, K, dist, seed = workload(name)
-        A, B = operands(M, N, K, dist, seed)
-        _DEVICE_OPERANDS[name] = (torch.from_numpy(A.view(np.int16)).cuda(),
-                                  torch.from_numpy(B.view(np.int16)).cuda(),
-                                  torch.empty((M, N), dtype=torch.int16, device="cuda"))
-    return _DEVICE_OPERANDS[name]
+        _, M, N, K, wdist, seed = workload(name)
+        A, B = operands(M, N, K, dist or wdist, seed)
+        _DEVICE_OPERANDS[key] = (torch.from_numpy(A.view(np.int16)).cuda(),
+                                 torch.from_numpy(B.view(np.int16)).cuda(),
+                                 torch.empty((M, N), dtype=torch.int16, device="cuda"))
+    return _DEVICE_OPERANDS[key]
 
 
 def layout_views(torch, A, B, C, layout):
@@ -107,11 +112,11 @@ def layout_views(torch, A, B, C, layout):
     return A, B, C
 
 
-def time_workload(g, torch, name, steps, warmup, opts, layout="nn"):
+def time_workload(g, torch, name, steps, warmup, opts, layout="nn", dist=None):
     from synthetic_inputs import workload
 
     _, M, N, K, _, _ = workload(name)
-    Ad, Bd, Cd = layout_views(torch, *device_operands(torch, name), layout)
+    Ad, Bd, Cd = layout_views(torch, *device_operands(torch, name, dist), layout)
     rc, plan = g.gemm_f16f32_strided_plan(M, N, K, Ad.data_ptr(), *Ad.stride(), Bd.data_ptr(),
                                           *Bd.stride(), Cd.data_ptr(), *Cd.stride(),
                                           opts=opts or None)
@@ -210,42 +215,55 @@ def copy_calibration(torch, mib, steps):
                       "GB_per_s": round(2 * n / dt / 1e9, 1)}), flush=True)
 
 
-def gfx_clocks_mhz():
-    """Current GFX clock of every XCD from `amd-smi metric -c` (empty list if unavailable)."""
+def parse_smi(text):
+    """(GFX clock of every XCD in MHz, socket power in W or None) from the text of
+    `amd-smi metric -c -p`: the CLK line of each GFX_<n> block, and the SOCKET_POWER line."""
     import re
-    import subprocess
-    try:
-        out = subprocess.run(["amd-smi", "metric", "-c"], capture_output=True, text=True,
-                             timeout=10).stdout
-    except (OSError, subprocess.SubprocessError):
-        return []
-    clocks, in_gfx = [], False
-    for line in out.splitlines():
+    clocks, in_gfx, power = [], False, None
+    for line in text.splitlines():
         if re.match(r"\s*GFX_\d+:\s*$", line):
             in_gfx = True
             continue
         m = re.match(r"\s*CLK:\s*(\d+)", line)
+        p = re.match(r"\s*SOCKET_POWER:\s*([\d.]+)", line)
         if in_gfx and m:
             clocks.append(int(m.group(1)))
             in_gfx = False
+        elif p:
+            power = float(p.group(1))
         elif line.strip().endswith(":"):
             in_gfx = False
-    return clocks
+    return clocks, power
+
+
+def smi_sample():
+    """Current XCD clocks and socket power (parse_smi of one `amd-smi metric -c -p`; [] and
+    None if amd-smi is unavailable)."""
+    import subprocess
+    try:
+        out = subprocess.run(["amd-smi", "metric", "-c", "-p"], capture_output=True, text=True,
+                             timeout=10).stdout
+    except (OSError, subprocess.SubprocessError):
+        return [], None
+    return parse_smi(out)
 
 
 def sample_clocks(g, torch, fn, seconds=3.0):
     """Runs fn back to back for `seconds` (untimed, after the timed region) while sampling the
-    XCD clocks; returns the 5th percentile, median and 95th percentile in MHz over all samples
-    and XCDs, or None."""
+    XCD clocks and the socket power; returns the 5th percentile, median and 95th percentile
+    in MHz over all samples and XCDs, and the median socket power in W, or None."""
     import threading
-    samples, done = [], threading.Event()
+    samples, powers, done = [], [], threading.Event()
 
     def poll():
         while not done.is_set():
-            samples.extend(gfx_clocks_mhz())
+            c, pw = smi_sample()
+            samples.extend(c)
+            if pw is not None:
+                powers.append(pw)
             time.sleep(0.2)
 
-    if not gfx_clocks_mhz():
+    if not smi_sample()[0]:
         return None
     for _ in range(20):          # the clocks ramp up before sampling starts
         fn()
@@ -277,7 +295,9 @@ def sample_clocks(g, torch, fn, seconds=3.0):
     q = lambda f: samples[min(len(samples) - 1, int(f * len(samples)))]
     # an XCD occasionally reads a few hundred MHz for an instant; percentiles keep such
     # outliers from standing for the run
-    return {"p05": q(0.05), "median": q(0.5), "p95": q(0.95), "samples": len(samples)}
+    powers.sort()
+    return {"p05": q(0.05), "median": q(0.5), "p95": q(0.95), "samples": len(samples),
+            "socket_power_w": powers[len(powers) // 2] if powers else None}
 
 
 def cpu_all():
@@ -367,6 +387,8 @@ def main():
                     help="storage of A, B[, C]: n = row-major, t = column-major (e.g. nt)")
     ap.add_argument("--layouts", action="store_true",
                     help="time every storage order of A, B and C (stderr)")
+    ap.add_argument("--dist", default=None,
+                    help="operand distribution instead of the workload's (e.g. zeros, s(1/64))")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sweep", action="store_true",
                     help="time GROUP_SIZE_M in 1..32 with the XCD permutation on and off (stderr)")
@@ -391,7 +413,7 @@ def main():
 
     import torch
     import dense_gemm_f16f32_amd as g
-    from synthetic_inputs import WORKLOADS
+    from synthetic_inputs import WORKLOADS, workload
 
     torch.cuda.set_device(0)
     if args.copy_mib:
@@ -434,14 +456,17 @@ def main():
         print(json.dumps(time_torch(torch, args.workload, args.steps, args.warmup)),
               file=sys.stderr, flush=True)
 
-    r = time_workload(g, torch, args.workload, args.steps, args.warmup, opts, args.layout)
+    r = time_workload(g, torch, args.workload, args.steps, args.warmup, opts, args.layout,
+                      args.dist)
     plan = r["plan"]
     clocks = None
     if not args.no_clocks:
-        Ad, Bd, Cd = layout_views(torch, *device_operands(torch, args.workload), args.layout)
+        Ad, Bd, Cd = layout_views(torch, *device_operands(torch, args.workload, args.dist),
+                                  args.layout)
         clocks = sample_clocks(g, torch, lambda: g.matmul(Ad, Bd, Cd, **opts))
+    # the counters were taken on the workload's own operands in row-major storage
     traffic = (measured_traffic(args.workload, plan["tile"], plan["group_m"], plan["xcd_remap"])
-               if args.layout == "nn" else None)
+               if args.layout == "nn" and args.dist is None else None)
     out = {
         "metric": METRIC,
         "value": round(r["value"], 2),
@@ -457,6 +482,7 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": args.workload, "M": r["M"], "N": r["N"], "K": r["K"],
+            "dist": args.dist or workload(args.workload)[4],
             "accumulate": "f32", "layout": args.layout,
             "path": ["dma", "generic"][plan["path"]],
             "tile": f"{plan['bm']}x{plan['bn']}x{plan['bk']}", "tile_id": plan["tile"],
@@ -473,8 +499,9 @@ def main():
             "traffic": traffic,
             "kernel_ms": {k: round(r["kernel_ms_" + k], 5) for k in ("mean", "median", "min",
                                                                       "p90")},
-            # XCD clocks while the same launches run back to back (3 s after the timed region)
-            # and the dense fp16 peak at their median: 256 CUs x 4096 flop/clk x f
+            # XCD clocks (and socket power) while the same launches run back to back (3 s after
+            # the timed region) and the dense fp16 peak at their median: 256 CUs x 4096 flop/clk
+            # x f
             "sclk_mhz": clocks,
             "peak_at_sclk": (round(256 * 4096 * clocks["median"] * 1e6 / 1e12, 1)
                              if clocks else None),

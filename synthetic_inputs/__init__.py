@@ -22,6 +22,12 @@ Distributions (each value is an IEEE binary16 bit pattern, returned as uint16):
   * "n(0,0.1)": Box-Muller in float64 on the pair of draws (2*floor(t/2), 2*floor(t/2)+1),
     cos branch for even t, sin branch for odd t, times 0.1, then numpy's float64 -> float16
     conversion (round to nearest even).  Uniforms for Box-Muller are ((z >> 11) + 0.5) / 2^53.
+
+Two low-switching-activity distributions, for measuring how much of the GEMM's time is set by
+the data-dependent power of the matrix cores (same shapes, same memory traffic):
+  * "zeros": every value +0 (no draw is made).
+  * "s(1/64)": +1/64 or -1/64, the sign taken from the top bit of the draw: one bit of each
+    operand changes from value to value.
 """
 from __future__ import annotations
 
@@ -35,6 +41,7 @@ _M1 = np.uint64(0xBF58476D1CE4E5B9)
 _M2 = np.uint64(0x94D049BB133111EB)
 
 DISTS = ("u(-0.5,0.5)", "u(0,1)", "n(0,0.1)")
+LOW_ACTIVITY_DISTS = ("zeros", "s(1/64)")
 
 # Draws are produced in chunks so that 8192x8192 operands do not need a 1 GiB temporary.
 _CHUNK = 1 << 22
@@ -80,7 +87,13 @@ def _values(dist: str, seed: int, start: int, count: int) -> np.ndarray:
         ang = 2.0 * np.pi * u2
         v = np.where(t % 2 == 0, r * np.cos(ang), r * np.sin(ang)) * 0.1
         return v.astype(np.float16).view(np.uint16)
-    raise ValueError(f"unknown distribution {dist!r}; expected one of {DISTS}")
+    if dist == "zeros":
+        return np.zeros(count, dtype=np.uint16)
+    if dist == "s(1/64)":
+        sign = (splitmix64(seed, start, count) >> np.uint64(63)).astype(np.uint16)
+        return np.uint16(0x2400) | (sign << np.uint16(15))   # 0x2400 = 1/64 in binary16
+    raise ValueError(f"unknown distribution {dist!r}; expected one of "
+                     f"{DISTS + LOW_ACTIVITY_DISTS}")
 
 
 def stream(dist: str, seed: int, start: int, count: int) -> np.ndarray:

@@ -46,3 +46,28 @@ def test_source_hash_ignores_comments():
     assert bench.strip_comments(code) == bench.strip_comments(
         "int f(int x) { return x + 1; }")
     assert bench.strip_comments(code) != bench.strip_comments("int f(int x) { return x + 2; }")
+
+
+def test_smi_parser():
+    # the layout `amd-smi metric -c -p` prints (ROCm 7): a POWER block, then one block per
+    # clock domain; only the GFX_<n> clocks and the socket power are taken
+    text = """GPU: 0
+    POWER:
+        SOCKET_POWER: 1399 W
+        GFX_VOLTAGE: N/A
+    CLOCK:
+        GFX_0:
+            CLK: 1745 MHz
+            MIN_CLK: 500 MHz
+            MAX_CLK: 2400 MHz
+        GFX_1:
+            CLK: 1762 MHz
+            MAX_CLK: 2400 MHz
+        MEM_0:
+            CLK: 2000 MHz
+            MIN_CLK: 2000 MHz
+        VCLK_0:
+            CLK: 29 MHz
+"""
+    assert bench.parse_smi(text) == ([1745, 1762], 1399.0)
+    assert bench.parse_smi("") == ([], None)

@@ -40,3 +40,17 @@ def test_b_continues_the_stream():
     A, B = operands(3, 4, 5, "u(0,1)", 1)
     s = stream("u(0,1)", 1, 0, 3 * 5 + 5 * 4)
     assert np.array_equal(A.ravel(), s[:15]) and np.array_equal(B.ravel(), s[15:])
+
+
+def test_low_activity_distributions():
+    A, B = operands(64, 32, 48, "zeros", 3)
+    assert not A.any() and not B.any()
+    A, B = operands(500, 300, 400, "s(1/64)", 3)
+    v = np.concatenate([A.ravel(), B.ravel()]).view(np.float16).astype(np.float64)
+    assert set(np.unique(v)) == {-1 / 64, 1 / 64}
+    assert abs(np.mean(v > 0) - 0.5) < 0.01
+    # the sign bit is the top bit of the same draws whose top 11 bits index the uniform grid
+    # (top bit set: grid index >= 1024, a value >= 0; here the negative value)
+    u = stream("u(-0.5,0.5)", 3, 0, 1000).view(np.float16)
+    s = stream("s(1/64)", 3, 0, 1000).view(np.float16)
+    assert np.array_equal(s < 0, u >= 0)
