@@ -795,8 +795,9 @@ __global__ void __launch_bounds__(256) splitk_reduce(const float* W, int64_t ldw
 // ---------------------------------------------------------------------------------------
 // Generic path: any leading dimension, any 2-byte alignment, any K, either storage order of
 // each operand.  Panels are fetched with raw buffer loads whose resource ends at the
-// matrix's last element, so reads past it return zero and never fault; chunks of a k-major
-// operand that reach k >= K are zeroed explicitly (x-major rows k >= K lie past the end).
+// matrix's last element, so reads past it return zero and never fault; the last panel's
+// slots with k >= K (chunks of a k-major operand, rows of an x-major one) are zeroed
+// explicitly.
 // kOdd: some row starts are only 2-byte aligned, so each 16-byte chunk is assembled from a
 // 4-byte-aligned dwordx4 plus one more dword and a byte funnel shift.
 // ---------------------------------------------------------------------------------------
@@ -844,6 +845,13 @@ __device__ __forceinline__ void generic_fetch(u32x4 (&v)[O::LD], const uint16_t*
     v[i] = load_chunk<kOdd>(r, 2u * ((uint32_t)row * (uint32_t)ld + (uint32_t)(c * 8)));
     if constexpr (O::KM) {
       if (tail) v[i] = mask_k(v[i], k0 + c * 8, K);
+    } else {
+      // Rows k >= K start past the matrix's last element, but the resource's extent is
+      // rounded up to a whole dword, which can admit the one element after it: with unpadded
+      // rows (ld = X) that is row K, x = 0.  Whatever it holds would be multiplied by the zero
+      // of the other operand at k = K, and Inf or NaN times zero is NaN, so those rows are
+      // zeroed like the k-major chunks past K.
+      if (tail && k0 + row >= K) v[i] = u32x4{0u, 0u, 0u, 0u};
     }
   }
 }

@@ -148,3 +148,30 @@ def test_thin_strips_in_every_order(M, N):
     for a_col, b_col in [(False, False), (True, False), (False, True), (True, True)]:
         got = call(place(A, a_col, pad=3), place(B, b_col, pad=3), output(M, N, False))
         assert np.array_equal(got, ref), (a_col, b_col)
+
+
+# Unpadded operands (ld equal to the stored row length) with NaN or Inf right after their last
+# element.  A buffer resource's extent is rounded up to a whole dword, so for an x-major operand
+# (B row-major, A column-major) with an odd number of elements from the last panel's corner it
+# admits that next element, at row k = K, x = 0; a path that stages rows k >= K must not let it
+# in, since Inf or NaN times the zero it meets there is NaN (row or column 0 of C would be NaN).
+# K is odd in every shape, and so is the x extent of at least one operand; (2, 1, 1301) is
+# planned with B as a 1-wide row-major operand.
+TIGHT_SHAPES = [(87, 317, 679), (2, 1, 1301), (649, 687, 215), (30, 341, 1), (563, 217, 1011),
+                (5, 7, 3)]
+
+
+@pytest.mark.parametrize("fill", [0x7E00, 0x7C00], ids=["nan", "inf"])
+@pytest.mark.parametrize("M,N,K", TIGHT_SHAPES)
+def test_unpadded_operands_ignore_what_follows_them(M, N, K, fill):
+    A, B = operands(M, N, K, "n(0,0.1)", 11 * M + N + K)
+    want = oracle.gemm(A, B)
+    for a_col, b_col, c_col in LAYOUTS:
+        Av = place(A, a_col, pad=0, fill=fill)
+        Bv = place(B, b_col, pad=0, fill=fill)
+        for generic in (0, 1):
+            what = f"{M}x{N}x{K} cols={a_col, b_col, c_col} generic={generic}"
+            Cv = output(M, N, c_col)
+            got = call(Av, Bv, Cv, force_generic=generic)
+            assert_within_tolerance(got, want, what)
+            assert padding_untouched(Cv, c_col), what

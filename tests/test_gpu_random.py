@@ -24,7 +24,7 @@ pytestmark = pytest.mark.gpu
 
 torch = pytest.importorskip("torch")
 
-CASES = 200
+CASES = 1000
 
 
 def log_uniform(rng, lo, hi):
