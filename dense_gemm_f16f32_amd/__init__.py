@@ -187,7 +187,8 @@ def _stream_handle(stream):
 def matmul(a, b, out=None, *, M=None, N=None, K=None, stream=None, workspace=None, **opts):
     """out[:M, :N] = fp16(a[:M, :K] @ b[:K, :N]) on the GPU (fp32 accumulation).
 
-    a, b, out: 2-D CUDA tensors of 16-bit elements (float16, or int16 holding fp16 bits),
+    a, b, out: 2-D CUDA tensors of float16 (or int16 / uint16 holding float16 bits; bfloat16
+    and other dtypes are refused),
     each row-major or column-major (one unit stride) with any leading dimension: transposed
     views such as `w.t()` are read in place.  opts: tile, group_m, xcd_remap, force_generic,
     split_edges, persistent, split_k (see include/gemm_f16f32.h).  Split K goes through
@@ -202,11 +203,16 @@ def matmul(a, b, out=None, *, M=None, N=None, K=None, stream=None, workspace=Non
     N = b.shape[1] if N is None else N
     if out is None:
         out = torch.empty((M, N), dtype=a.dtype, device=a.device)
+    fp16_bits = (torch.float16, torch.int16) + ((torch.uint16,) if hasattr(torch, "uint16")
+                                                  else ())
     for t in (a, b, out):
         if t.dim() != 2:
             raise ValueError("expected 2-D tensors")
-        if t.element_size() != 2 or not t.is_cuda:
-            raise ValueError("operands must be 16-bit CUDA tensors")
+        if t.dtype not in fp16_bits:   # bfloat16 is 2 bytes too, but not these bits
+            raise ValueError(f"operands must be float16 (or int16/uint16 holding float16 "
+                             f"bits), got {t.dtype}")
+    if not all(t.is_cuda for t in (a, b, out)):
+        raise ValueError("operands must be CUDA tensors")
     args = (M, N, K, a.data_ptr(), a.stride(0), a.stride(1), b.data_ptr(), b.stride(0),
             b.stride(1), out.data_ptr(), out.stride(0), out.stride(1))
     if workspace is not None and "split_k" not in opts:

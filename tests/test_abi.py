@@ -354,3 +354,15 @@ def test_struct_layouts_match_the_header(tmp_path):
         assert got[(cname, "size")] == ctypes.sizeof(py), cname
         for field, _ in py._fields_:
             assert got[(cname, field)] == getattr(py, field).offset, (cname, field)
+
+
+def test_matmul_refuses_other_dtypes_before_any_gpu_call():
+    torch = pytest.importorskip("torch")
+    f16 = torch.zeros((4, 4), dtype=torch.float16)
+    for dt in (torch.bfloat16, torch.float32, torch.int8):
+        bad = torch.zeros((4, 4), dtype=dt)
+        for args in ((bad, f16, f16), (f16, bad, f16), (f16, f16, bad)):
+            with pytest.raises(ValueError, match="float16"):
+                g.matmul(*args)
+    with pytest.raises(ValueError, match="CUDA"):   # right dtype, host memory
+        g.matmul(f16, f16, f16)
