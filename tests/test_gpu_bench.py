@@ -1,0 +1,51 @@
+"""bench.py end to end on the GPU: a short run prints one JSON line with the fields and types
+the benchmark contract names, consistent with each other (value from the timed steps, the
+roofline from per-launch event times, frac = achieved / peak)."""
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def run_bench(*args):
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), *args],
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stderr[-2000:]
+    lines = [ln for ln in r.stdout.splitlines() if ln.strip()]
+    assert len(lines) == 1, r.stdout
+    return json.loads(lines[0])
+
+
+@pytest.mark.parametrize("extra", [[], ["--dist", "zeros", "--workload", "gemm4096_u"]],
+                         ids=["default", "zeros-4096"])
+def test_bench_line_follows_the_contract(extra):
+    out = run_bench("--steps", "3", "--warmup", "1", "--no-cpu-baseline", "--no-clocks", *extra)
+    for key, typ in (("metric", str), ("value", float), ("unit", str), ("n_gpus", int),
+                     ("steps", int), ("warmup", int), ("ms_per_step", float),
+                     ("higher_is_better", bool), ("scaling", str), ("dtype", str),
+                     ("data", str), ("config", dict), ("roofline", dict)):
+        assert isinstance(out[key], typ), key
+    assert out["n_gpus"] == 1 and out["steps"] == 3 and out["warmup"] == 1
+    assert out["unit"] == "TFLOP/s" and out["higher_is_better"] is True
+    assert out["vs_baseline"] is None and out["cpu_baseline"] is None
+    cfg = out["config"]
+    M, N, K = cfg["M"], cfg["N"], cfg["K"]
+    assert abs(out["value"] - 2 * M * N * K / (out["ms_per_step"] * 1e-3) / 1e12) \
+        <= 1e-3 * out["value"] + 0.01
+    roof = out["roofline"]
+    assert roof["bound"] == "mfma" and roof["unit"] == "TFLOP/s" and roof["peak"] == 2500.0
+    assert abs(roof["frac"] - roof["achieved"] / roof["peak"]) < 1e-4
+    assert 0 < roof["frac"] < 1
+    if extra:
+        assert cfg["dist"] == "zeros" and (M, N, K) == (4096, 4096, 4096)
+        assert roof["traffic"] is None          # the counters were taken on other operands
+    else:
+        assert cfg["dist"] == "u(-0.5,0.5)" and (M, N, K) == (8192, 8192, 8192)
+        assert cfg["workload"] == "gemm8192_u" and cfg["tile"] == "256x256x64"
+        assert roof["traffic"] is None or roof["traffic"] > 2 * (M * K + K * N + M * N)
