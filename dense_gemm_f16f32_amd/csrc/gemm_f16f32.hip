@@ -178,13 +178,15 @@ struct Part {
 int plan_launch(const Problem& pr, int64_t M, int64_t N, const TileDesc* t, int group,
                 const gemm_f16f32_opts& o, gemm_f16f32_plan_info* r) {
   const int64_t kMax = (int64_t)1 << 31;
-  // 32-bit in-kernel offsets: one panel's stored rows of A (bm rows if k-major, else up to 64
-  // k rows) and of B (bn or 64), and one tile's bm rows of C.
-  const int64_t rows_a = pr.a_kmajor ? t->bm : gk::kBK, rows_b = pr.b_kmajor ? t->bn : gk::kBK;
+  const bool dma = !o.force_generic;
+  // 32-bit in-kernel offsets: one panel's stored rows of A (bm rows if k-major, else one k row
+  // per k value of the panel: the tile's BK on the DMA path, 64 on the generic one) and of B
+  // (bn, or the same k rows), and one tile's bm rows of C.
+  const int64_t depth = dma ? t->bk : gk::kBK;
+  const int64_t rows_a = pr.a_kmajor ? t->bm : depth, rows_b = pr.b_kmajor ? t->bn : depth;
   if (product_reaches(rows_a, pr.lda, kMax) || product_reaches(rows_b, pr.ldb, kMax) ||
       product_reaches(t->bm, pr.ldc, kMax))
     return GEMM_F16F32_ERR_TOO_LARGE;
-  const bool dma = !o.force_generic;
   r->path = dma ? GEMM_F16F32_PATH_DMA : GEMM_F16F32_PATH_GENERIC;
   r->tile = t->id;
   r->bm = t->bm;

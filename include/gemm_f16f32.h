@@ -58,7 +58,9 @@ enum {
     GEMM_F16F32_ERR_TOO_LARGE = -6, /* a leading dimension beyond the kernels' 32-bit offsets:
                                        BM * ldc, and for each operand (rows of one stored
                                        panel) * ld must stay below 2^31, where a panel has BM
-                                       (BN) rows when k is the unit-stride axis, else 64; with
+                                       (BN) rows when k is the unit-stride axis, else one row
+                                       per k value of the panel (the tile's BK, 32-128; 64 on
+                                       the generic path); with
                                        split K also BM * ldw * 4 bytes, M * ldw / 4 and the
                                        grid splits * programs (ldw = N rounded up to 4) */
     GEMM_F16F32_ERR_HIP = -7,       /* the HIP runtime rejected the launch */

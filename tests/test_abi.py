@@ -295,6 +295,14 @@ def test_too_large_c_leading_dimension():
     # a transposed operand's panel spans 64 k rows: 64 x lda
     assert splan(8, 8, 8, (1, 1 << 25), (8, 1), (8, 1), a=1 << 40, b=2 << 40,
                  c=3 << 40)[0] == g.ERR_TOO_LARGE
+    # ... and 128 with a 128-deep tile: at ld = 2^24 + 8 that is past 2^31 for B row-major
+    # (x-major), within it for the 64-deep tiles and the generic path (64 rows)
+    ld = (1 << 24) + 8
+    args = (8, 8, 8, 1 << 40, 2 << 40, 3 << 40, 8, ld, 8)
+    assert g.gemm_f16f32_plan(*args, opts={"tile": g.TILE_32x64x128})[0] == g.ERR_TOO_LARGE
+    assert g.gemm_f16f32_plan(*args, opts={"tile": g.TILE_32x64x64})[0] == g.OK
+    assert g.gemm_f16f32_plan(*args, opts={"tile": g.TILE_32x64x128,
+                                           "force_generic": 1})[0] == g.OK
 
 
 def test_persistent_plans():
