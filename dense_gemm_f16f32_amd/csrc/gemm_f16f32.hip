@@ -320,9 +320,19 @@ int plan_parts(const Problem& pr, const gemm_f16f32_opts* opts, int64_t ws_bytes
       if (rm > 0 && 4 * rm <= t->bm) Mm = M - rm;
     }
   }
+  // A tile chosen here (not forced by the caller) that cannot address the operands with
+  // 32-bit offsets -- a leading dimension of about 2^24 elements or more -- gives way to the
+  // 32 x 32 x 64 tile, whose panels store the fewest rows, before the call is refused.
+  auto plan_or_fallback = [&](int64_t m, int64_t n, const TileDesc* tt, int group, bool forced,
+                              const gemm_f16f32_opts& oo, gemm_f16f32_plan_info* r) {
+    int rc = plan_launch(pr, m, n, tt, group, oo, r);
+    if (rc == GEMM_F16F32_ERR_TOO_LARGE && !forced && tt->id != GEMM_F16F32_TILE_32x32x64)
+      rc = plan_launch(pr, m, n, find_tile(GEMM_F16F32_TILE_32x32x64), 0, oo, r);
+    return rc;
+  };
   Part* pp = parts;
   pp->m_off = 0, pp->n_off = 0, pp->M = Mm, pp->N = Nm;
-  int rc = plan_launch(pr, Mm, Nm, t, ch.group, o, &pp->r);
+  int rc = plan_or_fallback(Mm, Nm, t, ch.group, o.tile != 0, o, &pp->r);
   if (rc != GEMM_F16F32_OK) return rc;
   if (split_k) {
     *nparts = 1;
@@ -337,7 +347,7 @@ int plan_parts(const Problem& pr, const gemm_f16f32_opts* opts, int64_t ws_bytes
     if (st[2] == 0 || st[3] == 0) continue;
     pp->m_off = st[0], pp->n_off = st[1], pp->M = st[2], pp->N = st[3];
     const Choice cs = choose_tile(st[2], st[3], K, aligned);
-    rc = plan_launch(pr, st[2], st[3], find_tile(cs.tile), cs.group, os, &pp->r);
+    rc = plan_or_fallback(st[2], st[3], find_tile(cs.tile), cs.group, false, os, &pp->r);
     if (rc != GEMM_F16F32_OK) return rc;
     ++pp;
   }

@@ -303,6 +303,15 @@ def test_too_large_c_leading_dimension():
     assert g.gemm_f16f32_plan(*args, opts={"tile": g.TILE_32x64x64})[0] == g.OK
     assert g.gemm_f16f32_plan(*args, opts={"tile": g.TILE_32x64x128,
                                            "force_generic": 1})[0] == g.OK
+    # a tile the planner chose itself gives way to 32 x 32 x 64 instead: 32 x 32 x 4096 takes
+    # the 128-deep 32 x 64 tile from the table, and 32 x 32 x 64 at this ldb
+    rc, info = g.gemm_f16f32_plan(32, 32, 4096, 1 << 40, 2 << 40, 3 << 40, 4096, 32, 32)
+    assert rc == g.OK and info["tile"] == g.TILE_32x64x128
+    rc, info = g.gemm_f16f32_plan(32, 32, 4096, 1 << 40, 2 << 40, 3 << 40, 4096, ld, 32)
+    assert rc == g.OK and info["tile"] == g.TILE_32x32x64 and info["bk"] == 64
+    # beyond what any tile addresses, still refused
+    assert g.gemm_f16f32_plan(32, 32, 4096, 1 << 40, 2 << 40, 3 << 40, 4096, 1 << 25,
+                              32)[0] == g.ERR_TOO_LARGE
 
 
 def test_persistent_plans():

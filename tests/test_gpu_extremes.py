@@ -4,6 +4,8 @@
   with M = N = 64, unsplit and split K: every element against the oracle.
 * M or N = 10^6 with the other side 2..33 and short K: grids of tens of thousands of
   workgroups on a 1-D launch, the last tile row / column ragged, both storage orders of C.
+* A leading dimension of 2^24 + 8 elements (a 33.6 GB operand buffer), where the choice of
+  tile depends on the kernels' 32-bit offsets.
 The bar is the usual 1e-2 + 2^-10 |oracle| (matmul of phobos "03: Matrix multiplication":
 fp32 accumulation, one fp16 narrowing); unsplit results must not depend on the tile.
 """
@@ -47,3 +49,26 @@ def test_very_long_thin_c(M, N, K):
     Ct = torch.empty((N, M), dtype=torch.int16, device="cuda")
     g.matmul(Ad, Bd, Ct.t())
     assert np.array_equal(from_dev(Ct).T, got)
+
+
+def test_leading_dimension_past_a_deep_panels_offsets():
+    # B row-major with ldb = 2^24 + 8 (a 33.6 GB buffer, NaN outside B's 32 columns): one
+    # 128-deep panel spans 128 ldb > 2^31 elements, past the kernels' 32-bit offsets, while a
+    # 64-deep one does not.  The planner's own choice for 32 x 32 x 1000 is a 128-deep tile; it
+    # gives way to the 32 x 32 x 64 tile, and a forced 128-deep tile is refused.
+    M, N, K = 32, 32, 1000
+    ld = (1 << 24) + 8
+    A, B = operands(M, N, K, "n(0,0.1)", 23)
+    buf = torch.full((K * ld,), 0x7E00, dtype=torch.int16, device="cuda")
+    try:
+        Bv = buf.view(K, ld)[:, :N]
+        Bv.copy_(to_dev(B))
+        Ad = to_dev(A)
+        rc, info = g.gemm_f16f32_plan(M, N, K, Ad.data_ptr(), Bv.data_ptr(), 1 << 40, K, ld, N)
+        assert rc == g.OK and info["tile"] == g.TILE_32x32x64
+        assert_within_tolerance(from_dev(g.matmul(Ad, Bv)), oracle.gemm(A, B), "ldb 2^24+8")
+        with pytest.raises(g.GemmError):
+            g.matmul(Ad, Bv, tile=g.TILE_32x64x128)
+    finally:
+        del buf
+        torch.cuda.empty_cache()
