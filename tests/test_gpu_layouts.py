@@ -175,3 +175,24 @@ def test_unpadded_operands_ignore_what_follows_them(M, N, K, fill):
             got = call(Av, Bv, Cv, force_generic=generic)
             assert_within_tolerance(got, want, what)
             assert padding_untouched(Cv, c_col), what
+
+
+@pytest.mark.parametrize("tile", sorted(g.TILES))
+def test_identity_through_every_tile_and_order(tile):
+    # A I = A and I B = B exactly, for every storage order of A and B, on the DMA and the
+    # generic path: every element must travel through the LDS layouts (swizzles, transposing
+    # reads), the MFMA lane map and the store to its own place.  Sizes are ragged against
+    # every tile (200 rows, 136 = 2 x 64 + 8 k values, 72 columns).
+    M, K, N = 200, 136, 72
+    A, _ = operands(M, 1, K, "n(0,0.1)", 31)
+    _, B = operands(1, N, K, "n(0,0.1)", 37)
+    eye = np.eye(K, dtype=np.float16).view(np.uint16)
+    for a_col, b_col in itertools.product((False, True), repeat=2):
+        for generic in (0, 1):
+            what = f"tile {tile} cols={a_col, b_col} generic={generic}"
+            got = call(place(A, a_col, pad=1), place(eye, b_col, pad=3), output(M, K, False),
+                       tile=tile, force_generic=generic)
+            assert np.array_equal(got, A), "A I " + what
+            got = call(place(eye, a_col, pad=2), place(B, b_col), output(K, N, True),
+                       tile=tile, force_generic=generic)
+            assert np.array_equal(got, B), "I B " + what
