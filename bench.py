@@ -12,7 +12,8 @@ HIP events recorded on the stream the kernel is launched on (torch's current str
 `value` is TFLOP/s = 2 M N K K_steps / (timed wall time); `roofline.achieved` is
 2 M N K / (mean per-launch event time), against the MI355X published dense fp16 matrix
 peak of 2.5 PFLOP/s.  `cpu_baseline` times the CPU oracle (fp64 ascending-k sums, one
-rounding) on one 256-row band of the same product, using all host threads it gets.
+rounding) on one 512-row band of the same product (about 13 s on a 16-thread host), using
+all host threads it gets.
 --all prints one extra JSON line per workload to stderr, with the device time per launch
 from HIP-graph replays beside the per-launch event times.  --layout stores A, B (and C) row-
 major ("n") or column-major ("t"), e.g. "nt" for B given as an N x K matrix; --layouts times
@@ -352,7 +353,7 @@ def _oracle_single_thread_seconds(A, B):
     return float(out.strip().splitlines()[-1])
 
 
-def cpu_baseline(name: str, rows: int = 256):
+def cpu_baseline(name: str, rows: int = 512):
     import numpy as np
     import oracle
     from synthetic_inputs import operands, workload
