@@ -7,7 +7,7 @@ HIP events recorded on the stream the kernel is launched on (torch's current str
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--all]
                     [--tile T] [--group-m G] [--xcd-remap R] [--layout AB[C]]
-                    [--layouts] [--dist D] [--no-cpu-baseline]
+                    [--layouts] [--dist D] [--vs-torch] [--no-cpu-baseline]
 
 `value` is TFLOP/s = 2 M N K K_steps / (timed wall time); `roofline.achieved` is
 2 M N K / (mean per-launch event time), against the MI355X published dense fp16 matrix
@@ -176,12 +176,12 @@ def graph_device_us(torch, fn, n=20, reps=5):
     return sorted(res)[len(res) // 2]
 
 
-def time_torch(torch, name, steps, warmup):
+def time_torch(torch, name, steps, warmup, dist=None):
     """torch.matmul (the vendor BLAS) on the same fp16 operands, for context only."""
     from synthetic_inputs import workload
 
-    _, M, N, K, _, _ = workload(name)
-    Ad, Bd, _ = device_operands(torch, name)
+    _, M, N, K, wdist, _ = workload(name)
+    Ad, Bd, _ = device_operands(torch, name, dist)
     a, b = Ad.view(torch.float16), Bd.view(torch.float16)
     for _ in range(warmup):
         torch.matmul(a, b)
@@ -195,9 +195,52 @@ def time_torch(torch, name, steps, warmup):
     torch.cuda.synchronize()
     per = sorted(s.elapsed_time(e) for s, e in ev)
     mean = sum(per) / len(per)
-    return {"context": "torch.matmul", "workload": name,
+    return {"context": "torch.matmul", "workload": name, "dist": dist or wdist,
             "tflops": round(2.0 * M * N * K / (mean * 1e-3) / 1e12, 1),
             "kernel_ms_median": round(per[len(per) // 2], 4)}
+
+
+def vs_torch(g, torch, name, opts, dist=None, rounds=10, block=50, warm_s=3.0):
+    """Interleaved A/B against torch.matmul (the vendor BLAS), for context only: after warm_s
+    seconds of both, `rounds` rounds of one block of each (order alternating), per-launch HIP
+    events; the median over rounds of each block's mean launch time."""
+    import statistics
+    from synthetic_inputs import workload
+
+    _, M, N, K, wdist, _ = workload(name)
+    Ad, Bd, Cd = device_operands(torch, name, dist)
+    a, b = Ad.view(torch.float16), Bd.view(torch.float16)
+    fns = {"library": lambda: g.matmul(Ad, Bd, Cd, **opts),
+           "torch.matmul": lambda: torch.matmul(a, b)}
+    t_end = time.perf_counter() + warm_s
+    while time.perf_counter() < t_end:
+        for _ in range(10):
+            for fn in fns.values():
+                fn()
+        torch.cuda.synchronize()
+
+    def timed(fn):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(block)]
+        for s, e in ev:
+            s.record()
+            fn()
+            e.record()
+        torch.cuda.synchronize()
+        return sum(s.elapsed_time(e) for s, e in ev) / block
+
+    res = {k: [] for k in fns}
+    for r in range(rounds):
+        for k in (list(fns) if r % 2 == 0 else list(fns)[::-1]):
+            res[k].append(timed(fns[k]))
+    out = {"ab": "interleaved", "workload": name, "dist": dist or wdist, "rounds": rounds,
+           "block": block}
+    for k, v in res.items():
+        med = statistics.median(v)
+        out[k] = {"ms_median": round(med, 5), "ms_min": round(min(v), 5),
+                  "ms_max": round(max(v), 5),
+                  "tflops": round(2.0 * M * N * K / (med * 1e-3) / 1e12, 1)}
+    return out
 
 
 def copy_calibration(torch, mib, steps):
@@ -393,8 +436,11 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sweep", action="store_true",
                     help="time GROUP_SIZE_M in 1..32 with the XCD permutation on and off (stderr)")
+    ap.add_argument("--vs-torch", action="store_true",
+                    help="interleaved A/B against torch.matmul after a warm-up (stderr)")
     ap.add_argument("--torch", action="store_true",
-                    help="also time torch.matmul on the same operands (stderr, context only)")
+                    help="also time torch.matmul on the same operands (stderr, context only; "
+                         "it runs before the library's timed steps, so --vs-torch compares)")
     ap.add_argument("--no-clocks", action="store_true",
                     help="skip the 3 s clock sampling after the timed region")
     ap.add_argument("--cpu-all", action="store_true",
@@ -454,8 +500,11 @@ def main():
                               "kernel_ms_median": round(rr["kernel_ms_median"], 4)}),
                   file=sys.stderr, flush=True)
     if args.torch:
-        print(json.dumps(time_torch(torch, args.workload, args.steps, args.warmup)),
+        print(json.dumps(time_torch(torch, args.workload, args.steps, args.warmup, args.dist)),
               file=sys.stderr, flush=True)
+    if args.vs_torch:
+        print(json.dumps(vs_torch(g, torch, args.workload, opts, args.dist)), file=sys.stderr,
+              flush=True)
 
     r = time_workload(g, torch, args.workload, args.steps, args.warmup, opts, args.layout,
                       args.dist)
