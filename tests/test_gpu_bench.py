@@ -49,3 +49,19 @@ def test_bench_line_follows_the_contract(extra):
         assert cfg["dist"] == "u(-0.5,0.5)" and (M, N, K) == (8192, 8192, 8192)
         assert cfg["workload"] == "gemm8192_u" and cfg["tile"] == "256x256x64"
         assert roof["traffic"] is None or roof["traffic"] > 2 * (M * K + K * N + M * N)
+
+
+def test_vs_torch_reports_both_sides():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--vs-torch",
+                        "--workload", "gemm4096_u", "--steps", "2", "--warmup", "1",
+                        "--no-cpu-baseline", "--no-clocks"],
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stderr[-2000:]
+    ab = [json.loads(ln) for ln in r.stderr.splitlines() if ln.startswith('{"ab"')]
+    assert len(ab) == 1, r.stderr[-2000:]
+    ab = ab[0]
+    assert ab["workload"] == "gemm4096_u" and ab["rounds"] == 10 and ab["block"] == 50
+    for side in ("library", "torch.matmul"):
+        t = ab[side]
+        assert 0 < t["ms_min"] <= t["ms_median"] <= t["ms_max"]
+        assert abs(t["tflops"] - 2 * 4096 ** 3 / (t["ms_median"] * 1e-3) / 1e12) < 0.1 + 1e-3 * t["tflops"]
