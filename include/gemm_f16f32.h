@@ -60,9 +60,11 @@ enum {
                                        panel) * ld must stay below 2^31, where a panel has BM
                                        (BN) rows when k is the unit-stride axis, else one row
                                        per k value of the panel (the tile's BK, 32-128; 64 on
-                                       the generic path); with
-                                       split K also BM * ldw * 4 bytes, M * ldw / 4 and the
-                                       grid splits * programs (ldw = N rounded up to 4) */
+                                       the generic path); with split K also BM * ldw * 4
+                                       bytes, M * ldw / 4 and the grid splits * programs
+                                       (ldw = N rounded up to 4).  A tile the library chose
+                                       that fails this gives way to the 32 x 32 x 64 tile
+                                       first; a forced tile does not. */
     GEMM_F16F32_ERR_HIP = -7,       /* the HIP runtime rejected the launch */
     GEMM_F16F32_ERR_WORKSPACE = -8  /* split K planned but no workspace (an entry point without
                                        one), or the workspace is smaller than
