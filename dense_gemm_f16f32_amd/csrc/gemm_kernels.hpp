@@ -432,16 +432,17 @@ __device__ __forceinline__ void slot_offsets(uint32_t (&off)[O::LD], int w, int 
   }
 }
 
-// Full panel at (x0, k0), k0 >= 0: 16-byte DMA into the operand's part of a stage.  A panel
-// that is not live gets an empty resource: its loads touch no memory and deposit zeros.
-template <class O>
+// Full panel at (x0, k0), k0 >= 0: 16-byte DMA into the operand's part of a stage (load slots
+// I0 <= i < I1 of each thread; all of them by default).  A panel that is not live gets an empty
+// resource: its loads touch no memory and deposit zeros.
+template <class O, int I0 = 0, int I1 = O::LD>
 __device__ __forceinline__ void dma_panel(const uint16_t* ptr, int64_t ld, int64_t ext, int x0,
                                           int64_t k0, bool live, const uint32_t (&off)[O::LD],
                                           char GK_LDS* dst, int w) {
   const int64_t e0 = elem_off<O::KM>(x0, k0, ld);
   const __amdgpu_buffer_rsrc_t r = make_rsrc(ptr + (live ? e0 : 0), live ? 2 * (ext - e0) : 0);
 #pragma unroll
-  for (int i = 0; i < O::LD; ++i)
+  for (int i = I0; i < I1; ++i)
     buffer_load_lds16(r, (void GK_LDS*)(dst + (i * O::NW + w) * 1024), off[i]);
 }
 
@@ -575,6 +576,8 @@ __device__ __forceinline__ void dma_tile(const Args& p, int m0, int n0,
   constexpr int NM = T::TM * T::TN;        // MFMAs per k step
   constexpr int ND = OA::READS + OB::READS;  // LDS reads per k step
   constexpr int NV = T::A_LD + T::B_LD;    // buffer->LDS loads per panel
+  // NS == 2, RD == 1: a quarter of each refill is issued one k step later (see `panel`)
+  constexpr bool kSplitRefill = NS == 2 && RD == 1 && T::B_LD >= 2;
   static_assert(KS % 2 == 0 && NS >= 2 && NS <= kMaxStages, "pipeline shape");
   static_assert(NS * T::STAGE <= 160 * 1024, "LDS");
   static_assert((NS - 2) * NV <= 63, "vmcnt range");
@@ -614,12 +617,19 @@ __device__ __forceinline__ void dma_tile(const Args& p, int m0, int n0,
     if (patch_b >= 0) *(uint16_t GK_LDS*)(base + T::A_BYTES + patch_b) = last_b;
   };
 
-  // Full panel s (k0 = kofs + s BK >= 0) into `base`; panels s >= np load zeros.
-  auto issue = [&](int s, char GK_LDS* base) __attribute__((always_inline)) {
+  // Full panel s (k0 = kofs + s BK >= 0) into `base`; panels s >= np load zeros.  `part`
+  // splits it: 1 = A's slots and the first half of B's, 2 = the rest of B's (0 = all).
+  constexpr int kBHalf = T::B_LD / 2;
+  auto issue = [&](int s, char GK_LDS* base, int part = 0) __attribute__((always_inline)) {
     const bool live = s < np;
     const int64_t k0 = (int64_t)kofs + (int64_t)s * BK;
-    dma_panel<OA>(p.A, p.lda, extA, m0, k0, live, offA, base, w);
-    dma_panel<OB>(p.B, p.ldb, extB, n0, k0, live, offB, base + T::A_BYTES, w);
+    if (part != 2) dma_panel<OA>(p.A, p.lda, extA, m0, k0, live, offA, base, w);
+    if (part == 0)
+      dma_panel<OB>(p.B, p.ldb, extB, n0, k0, live, offB, base + T::A_BYTES, w);
+    else if (part == 1)
+      dma_panel<OB, 0, kBHalf>(p.B, p.ldb, extB, n0, k0, live, offB, base + T::A_BYTES, w);
+    else
+      dma_panel<OB, kBHalf, T::B_LD>(p.B, p.ldb, extB, n0, k0, live, offB, base + T::A_BYTES, w);
   };
 
   // Head panel (k0 = kofs < 0).
@@ -647,7 +657,12 @@ __device__ __forceinline__ void dma_tile(const Args& p, int m0, int n0,
   // `prev` held panel s-1.  K step kk multiplies the operands of step kk and reads those of
   // step kk + RD, which from kk = KS - RD on lie in panel s+1: that is where this panel's
   // barrier sits (after it every wave has read all of panel s, and panel s+1 has landed).
-  //  * NS == 2: right past the barrier, `cur` is refilled with panel s+2.
+  //  * NS == 2: right past the barrier, `cur` is refilled with panel s+2.  With RD == 1 the
+  //    barrier sits in the last k step, which then also issues 16 MFMAs, the next panel's first
+  //    operand reads and the refill; a quarter of the refill (the second half of B's slots) is
+  //    moved to the first k step of panel s+1, which thins that step out and still leaves the
+  //    loads three k steps before they are waited for (measured: 1.2 % faster at 8192^3 on
+  //    random and on all-zero operands, same results).
   //  * NS >= 3: `prev` is refilled with panel s+NS-1 at the start of the panel, its loads
   //    spread over the first k step's MFMAs.  Every wave finished reading `prev` before the
   //    previous panel's barrier (which waits for the wave's own LDS reads), so no further
@@ -659,11 +674,16 @@ __device__ __forceinline__ void dma_tile(const Args& p, int m0, int n0,
       if constexpr (NS >= 3) {
         if (kk == 0) issue(s + NS - 1, prev);
       }
+      if constexpr (kSplitRefill) {
+        // the rest of panel s+1's refill, started at the previous panel's barrier (panel 1 was
+        // loaded whole before the loop)
+        if (kk == 0 && s > 0) issue(s + 1, nxt, 2);
+      }
       if (kk == KS - RD) {
         wait_vmcnt<(NS - 2) * NV>();   // panel s+1 has landed (this wave's part)
         if (has_last && s + 2 == np) patch(nxt);   // panel s+1 is the last one
         lds_barrier();                 // ... every wave's part
-        if constexpr (NS == 2) issue(s + NS, cur);
+        if constexpr (NS == 2) issue(s + NS, cur, kSplitRefill ? 1 : 0);
       }
       const int ka = kk + RD;
       if (ka < KS)
@@ -671,11 +691,24 @@ __device__ __forceinline__ void dma_tile(const Args& p, int m0, int n0,
       else
         read_frags<T>(f[(j * KS + ka) % (RD + 1)], nxt, lo, ka - KS);
       mfma_step<T>(acc, f[(j * KS + kk) % (RD + 1)]);
-      const bool loads = NS >= 3 ? kk == 0 : kk == KS - RD;
-      if (loads)
-        sched_step<NM, ND, NV>();
-      else
-        sched_step<NM, ND, 0>();
+      if constexpr (NS >= 3) {
+        if (kk == 0)
+          sched_step<NM, ND, NV>();
+        else
+          sched_step<NM, ND, 0>();
+      } else if constexpr (kSplitRefill) {
+        if (kk == KS - RD)
+          sched_step<NM, ND, T::A_LD + kBHalf>();
+        else if (kk == 0)
+          sched_step<NM, ND, T::B_LD - kBHalf>();
+        else
+          sched_step<NM, ND, 0>();
+      } else {
+        if (kk == KS - RD)
+          sched_step<NM, ND, NV>();
+        else
+          sched_step<NM, ND, 0>();
+      }
     }
   };
 
