@@ -662,7 +662,9 @@ __device__ __forceinline__ void dma_tile(const Args& p, int m0, int n0,
   //    operand reads and the refill; a quarter of the refill (the second half of B's slots) is
   //    moved to the first k step of panel s+1, which thins that step out and still leaves the
   //    loads three k steps before they are waited for (measured: 1.2 % faster at 8192^3 on
-  //    random and on all-zero operands, same results).
+  //    random and on all-zero operands, same results).  Moving more of it one k step later,
+  //    or part of it two k steps later, measured slower at 8192^3 on low-activity data, where
+  //    the clock is highest and the loads run out of slack.
   //  * NS >= 3: `prev` is refilled with panel s+NS-1 at the start of the panel, its loads
   //    spread over the first k step's MFMAs.  Every wave finished reading `prev` before the
   //    previous panel's barrier (which waits for the wave's own LDS reads), so no further
