@@ -196,21 +196,28 @@ def matmul(a, b, out=None, *, M=None, N=None, K=None, stream=None, workspace=Non
     `workspace` (a CUDA tensor) is given, split_k then defaulting to SPLIT_K_AUTO.  A needed
     workspace that is not given is allocated by torch for this call.  Raises GemmError on a
     non-zero return code.  Launches on torch's current stream unless `stream` is given.
+    The M x K, K x N and M x N blocks must lie inside a, b and out (ValueError otherwise):
+    the library sees only pointers and strides, so it cannot check a tensor's extent.
     """
     import torch
-    M = a.shape[0] if M is None else M
-    K = a.shape[1] if K is None else K
-    N = b.shape[1] if N is None else N
-    if out is None:
-        out = torch.empty((M, N), dtype=a.dtype, device=a.device)
     fp16_bits = (torch.float16, torch.int16) + ((torch.uint16,) if hasattr(torch, "uint16")
                                                   else ())
-    for t in (a, b, out):
+    for t in (a, b) if out is None else (a, b, out):
         if t.dim() != 2:
             raise ValueError("expected 2-D tensors")
         if t.dtype not in fp16_bits:   # bfloat16 is 2 bytes too, but not these bits
             raise ValueError(f"operands must be float16 (or int16/uint16 holding float16 "
                              f"bits), got {t.dtype}")
+    M = a.shape[0] if M is None else M
+    K = a.shape[1] if K is None else K
+    N = b.shape[1] if N is None else N
+    if out is None:
+        out = torch.empty((max(M, 0), max(N, 0)), dtype=a.dtype, device=a.device)
+    # Negative sizes are left to the library, which returns ERR_DIM for them.
+    for t, rows, cols, what in ((a, M, K, "a"), (b, K, N, "b"), (out, M, N, "out")):
+        if rows > t.shape[0] or cols > t.shape[1]:
+            raise ValueError(f"{what} is {tuple(t.shape)}; the call needs its first "
+                             f"{rows} x {cols} block (M={M}, N={N}, K={K})")
     if not all(t.is_cuda for t in (a, b, out)):
         raise ValueError("operands must be CUDA tensors")
     args = (M, N, K, a.data_ptr(), a.stride(0), a.stride(1), b.data_ptr(), b.stride(0),

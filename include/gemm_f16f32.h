@@ -28,9 +28,9 @@
  *
  * Ownership and execution: A, B, C (and the split-K workspace of gemm_f16f32_strided_ws) are
  * device pointers owned by the caller.  The library allocates nothing and keeps no state
- * between calls, so calls from several host threads are safe.  A call checks its arguments, launches on `stream` (a hipStream_t; NULL is the null
- * stream) and returns without waiting; faults inside a kernel surface at the caller's next
- * synchronisation.  Only C[i][j] with i < M, j < N is written (padding between N and ldc is
+ * between calls, so calls from several host threads are safe.  A call checks its arguments,
+ * launches on `stream` (a hipStream_t; NULL is the null stream) and returns without waiting;
+ * faults inside a kernel surface at the caller's next synchronisation.  Only C[i][j] with i < M, j < N is written (padding between N and ldc is
  * left as it was).  M == 0 or N == 0 is a successful no-op; K == 0 writes +0 to the M x N
  * block.
  *

@@ -383,3 +383,29 @@ def test_matmul_refuses_other_dtypes_before_any_gpu_call():
                 g.matmul(*args)
     with pytest.raises(ValueError, match="CUDA"):   # right dtype, host memory
         g.matmul(f16, f16, f16)
+
+
+def test_matmul_refuses_blocks_outside_the_tensors_before_any_gpu_call():
+    """The library sees pointers and strides only; the binding checks that the M x K, K x N
+    and M x N blocks lie inside a, b and out (host tensors here: the check comes first)."""
+    torch = pytest.importorskip("torch")
+    z = lambda r, c: torch.zeros((r, c), dtype=torch.float16)
+    bad = [((z(4, 8), z(7, 5), z(4, 5)), {}),                 # b has fewer rows than K
+           ((z(4, 8), z(8, 5), z(3, 5)), {}),                 # out has fewer rows than M
+           ((z(4, 8), z(8, 5), z(4, 4)), {}),                 # out has fewer columns than N
+           ((z(4, 8), z(8, 5), z(4, 5)), dict(M=5)),
+           ((z(4, 8), z(8, 5), z(4, 5)), dict(K=9)),
+           ((z(4, 8), z(8, 5), z(4, 5)), dict(N=6)),
+           ((z(4, 8), z(8, 5).t(), z(4, 5)), {})]             # b.t() is 5 x 8
+    for args, sizes in bad:
+        with pytest.raises(ValueError, match="block"):
+            g.matmul(*args, **sizes)
+    # blocks inside larger tensors, and empty ones, pass on to the device check
+    for args, sizes in [((z(4, 8), z(9, 5), z(6, 7)), {}),
+                        ((z(4, 8), z(8, 5), z(4, 5)), dict(M=2, N=3, K=1)),
+                        ((z(0, 8), z(8, 5), z(0, 5)), {}),
+                        ((z(4, 0), z(0, 5), z(4, 5)), {})]:
+        with pytest.raises(ValueError, match="CUDA"):
+            g.matmul(*args, **sizes)
+    with pytest.raises(ValueError, match="CUDA"):      # out allocated for M x N
+        g.matmul(z(4, 8), z(8, 5))
