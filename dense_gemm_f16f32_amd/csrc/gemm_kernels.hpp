@@ -20,6 +20,10 @@
 // gfx950 specifics used here (each checked on the hardware with one-hot / index probes):
 //  * v_mfma_f32_32x32x16_f16: lane l supplies A[l%32][8(l/32) .. 8(l/32)+7] and
 //    B[8(l/32) .. +7][l%32]; result element v of lane l is C[8(v/4) + 4(l/32) + v%4][l%32].
+//  * v_mfma_f32_16x16x32_f16: lane l supplies A[l%16][8(l/16) .. +7] and B[8(l/16) .. +7][l%16];
+//    result element v of lane l is C[4(l/16) + v][l%16].  A 32-deep step of it gives the same
+//    fp32 result, bit for bit, as two 16-deep steps of the 32 x 32 instruction (checked on
+//    whole 8192^3 outputs), so every tile still yields the same bits.
 //  * ds_read_b64_tr_b16: inside each group of 16 lanes, lane i receives, as its 4 halves, the
 //    i-th 16-bit column of the 4 x 16 block whose row e is the 4 x 64 bits addressed by lanes
 //    4e .. 4e+3 of the group.  Panels stored with k as the row index therefore yield MFMA
@@ -39,6 +43,7 @@ namespace gk {
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef short short4v __attribute__((ext_vector_type(4)));
 typedef float float16v __attribute__((ext_vector_type(16)));
+typedef float float4v __attribute__((ext_vector_type(4)));
 typedef float float4v __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 #define GK_LDS __attribute__((address_space(3)))
@@ -86,7 +91,8 @@ __device__ __forceinline__ void program_tile(int h, int P, int num_pid_m, int nu
 // ---------------------------------------------------------------------------------------
 // Operands.  Both MFMA operands have the same register shape: lane l holds the 8 k values
 // 8(l/32) .. 8(l/32)+7 at position l % 32 along the operand's other axis X (the row of A, the
-// column of B).  They differ only in how the matrix is stored:
+// column of B) -- with 16x16x32 MFMAs (XB = 16) the 8 k values 8(l/16) .. +7 of a 32-deep step
+// at position l % 16.  They differ only in how the matrix is stored:
 //  * k-major (KM): consecutive k are adjacent in memory -- A row-major (M x K), or B stored
 //    transposed (N x K).  Element (x, k) is at x * ld + k.
 //  * x-major: consecutive x are adjacent -- B row-major (K x N), or A stored transposed
@@ -97,8 +103,9 @@ __device__ __forceinline__ void program_tile(int h, int P, int num_pid_m, int nu
 //    (ds_read_b64_tr_b16, 4 k rows each).
 // Chunk c of LDS row r sits at chunk position c ^ swz(r).
 // ---------------------------------------------------------------------------------------
-template <int BX_, int BK_, bool KM_, int W_, int NW_>
+template <int BX_, int BK_, bool KM_, int W_, int NW_, int XB_ = 32>
 struct Opnd {
+  static constexpr int XB = XB_, KD = XB_ == 32 ? 16 : 32;  // MFMA block width, k depth
   static constexpr int BX = BX_, BK = BK_;
   static constexpr bool KM = KM_;
   static constexpr int W = W_;                       // waves along X
@@ -109,10 +116,11 @@ struct Opnd {
   static constexpr int BYTES = BX * BK * 2;
   static constexpr int LD = BYTES / (NW * 64 * 16); // 16-byte loads per thread per panel
   static constexpr int WX = BX / W;                  // extent of one wave's block along X
-  static constexpr int T = WX / 32;                  // 32-wide MFMA blocks per wave
-  static constexpr int NOFF = KM ? BK / 16 : T;      // per-lane LDS read offsets
+  static constexpr int T = WX / XB;                  // MFMA blocks per wave
+  static constexpr int NOFF = KM ? BK / KD : T;      // per-lane LDS read offsets
   static constexpr int READS = KM ? T : 2 * T;       // LDS read instructions per k step
-  static_assert(T >= 1 && LD >= 1 && WX % 32 == 0, "operand tile too small for its waves");
+  static_assert(T >= 1 && LD >= 1 && WX % XB == 0, "operand tile too small for its waves");
+  static_assert(XB == 32 || !KM || CH >= 8, "16-row blocks keep the k-major swizzle");
   static_assert(!KM || CH == 16 || CH == 8 || CH == 4, "k-major LDS rows hold 128-32 halves");
   static_assert(KM || CH == 4 || CH == 8 || CH == 16 || CH == 32,
                 "x-major LDS rows hold 32-256 halves");
@@ -122,8 +130,14 @@ struct Opnd {
 template <int BM_, int BN_, int BK_, bool AKM, bool BKM, int WM_, int WN_>
 struct Tile {
   static constexpr int WM = WM_, WN = WN_, NW = WM * WN, NT = 64 * NW;  // waves, threads
-  using OA = Opnd<BM_, BK_, AKM, WM, NW>;
-  using OB = Opnd<BN_, BK_, BKM, WN, NW>;
+  // The 256 x 256 x 64 tile on 2 x 2 wavefronts issues 16x16x32 MFMAs (see `panel` in
+  // dma_tile): on random operands that instruction does more work per joule, and large GEMMs
+  // run at the board's power cap.  Every other tile keeps 32x32x16.
+  static constexpr bool M16 = BM_ == 256 && BN_ == 256 && BK_ == 64 && WM_ == 2 && WN_ == 2;
+  static constexpr int XB = M16 ? 16 : 32, KD = M16 ? 32 : 16, VN = M16 ? 4 : 16;
+  using Acc = std::conditional_t<M16, float4v, float16v>;
+  using OA = Opnd<BM_, BK_, AKM, WM, NW, XB>;
+  using OB = Opnd<BN_, BK_, BKM, WN, NW, XB>;
   static constexpr int BM = BM_, BN = BN_, BK = BK_;
   static constexpr int WTM = BM / WM, WTN = BN / WN; // per-wave block of C
   static constexpr int TM = OA::T, TN = OB::T;       // 32x32 MFMA blocks per wave
@@ -196,7 +210,10 @@ __device__ __forceinline__ int swz(int r) {
   } else if constexpr (O::CH == 4) {
     return 0;
   } else {
-    return ((0xE4A0 >> (4 * (r & 3))) & 0xF) & (O::CH - 1);
+    const int base = ((0xE4A0 >> (4 * (r & 3))) & 0xF) & (O::CH - 1);
+    if constexpr (O::XB == 16)
+      return base ^ ((((r >> 3) & 1) << 1) & (O::CH - 1));
+    return base;
   }
 }
 
@@ -230,8 +247,12 @@ template <class O>
 __device__ __forceinline__ void operand_offsets(int (&o)[O::NOFF], int wx, int lane, int base) {
   if constexpr (O::KM) {
 #pragma unroll
-    for (int kk = 0; kk < O::BK / 16; ++kk)
-      o[kk] = base + lds_chunk<O>(wx * O::WX + (lane & 31), kk * 2 + (lane >> 5));
+    for (int kk = 0; kk < O::BK / O::KD; ++kk) {
+      if constexpr (O::XB == 32)
+        o[kk] = base + lds_chunk<O>(wx * O::WX + (lane & 31), kk * 2 + (lane >> 5));
+      else
+        o[kk] = base + lds_chunk<O>(wx * O::WX + (lane & 15), kk * 4 + (lane >> 4));
+    }
   } else {
     // Lane 4e + j of a 16-lane group g addresses row (g/2)*8 + e and the 4 halves at
     // x = (g%2)*16 + 4j of its block: the group's 4 x 16 block then transposes into lane
@@ -239,8 +260,14 @@ __device__ __forceinline__ void operand_offsets(int (&o)[O::NOFF], int wx, int l
     const int g = lane >> 4, i = lane & 15;
 #pragma unroll
     for (int t = 0; t < O::T; ++t) {
-      const int x = wx * O::WX + t * 32 + (g & 1) * 16 + (i & 3) * 4;
-      o[t] = base + lds_chunk<O>((g >> 1) * 8 + (i >> 2), x >> 3) + ((x & 7) << 1);
+      if constexpr (O::XB == 32) {
+        const int x = wx * O::WX + t * 32 + (g & 1) * 16 + (i & 3) * 4;
+        o[t] = base + lds_chunk<O>((g >> 1) * 8 + (i >> 2), x >> 3) + ((x & 7) << 1);
+      } else {
+        // group g holds k = 8g .. 8g+7 of columns t*16 + 0..15
+        const int x = wx * O::WX + t * 16 + (i & 3) * 4;
+        o[t] = base + lds_chunk<O>(g * 8 + (i >> 2), x >> 3) + ((x & 7) << 1);
+      }
     }
   }
 }
@@ -258,9 +285,9 @@ template <class O>
 __device__ __forceinline__ half8 read_operand(const char GK_LDS* st, const int (&o)[O::NOFF],
                                               int t, int kk) {
   if constexpr (O::KM) {
-    return *(const half8 GK_LDS*)(st + o[kk] + t * 32 * O::ROW_BYTES);
+    return *(const half8 GK_LDS*)(st + o[kk] + t * O::XB * O::ROW_BYTES);
   } else {
-    const char GK_LDS* p = st + o[t] + kk * 16 * O::ROW_BYTES;
+    const char GK_LDS* p = st + o[t] + kk * O::KD * O::ROW_BYTES;
     short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((short4v GK_LDS*)p);
     short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((short4v GK_LDS*)(p + 4 * O::ROW_BYTES));
     return __builtin_bit_cast(half8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
@@ -277,21 +304,40 @@ __device__ __forceinline__ void read_frags(Frag<T>& f, const char GK_LDS* st,
   for (int tn = 0; tn < T::TN; ++tn) f.b[tn] = read_operand<typename T::OB>(st, o.b, tn, kk);
 }
 
+// One 16x16x32 MFMA accumulating in place on accumulator registers.  Written as inline asm:
+// through the builtin the compiler copied every 4-register accumulator once per MFMA.  The
+// compiler's hazard checks do not see inside the asm, so the code around it keeps the waits
+// the hardware needs: the accumulators are zeroed well before the first MFMA (a whole panel
+// prologue lies between) and read by the epilogue only after `mfma16_drain`.
+__device__ __forceinline__ void mfma16(float4v& acc, const half8& a, const half8& b) {
+  asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+
+// Wait states between the last MFMA written as asm and the first read of its result
+// (4 x 8, more than the longest such dependency of the 16x16x32 instruction).
+__device__ __forceinline__ void mfma16_drain() {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+}
+
 template <class T>
-__device__ __forceinline__ void mfma_step(float16v (&acc)[T::TM][T::TN], const Frag<T>& f) {
+__device__ __forceinline__ void mfma_step(typename T::Acc (&acc)[T::TM][T::TN], const Frag<T>& f) {
 #pragma unroll
   for (int tm = 0; tm < T::TM; ++tm)
 #pragma unroll
-    for (int tn = 0; tn < T::TN; ++tn)
-      acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.a[tm], f.b[tn], acc[tm][tn], 0, 0, 0);
+    for (int tn = 0; tn < T::TN; ++tn) {
+      if constexpr (T::M16)   // in place on accumulator registers (see mfma16)
+        mfma16(acc[tm][tn], f.a[tm], f.b[tn]);
+      else
+        acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.a[tm], f.b[tn], acc[tm][tn], 0, 0, 0);
+    }
 }
 
 // One whole staged panel, operands read just before use (generic path).
 template <class T>
-__device__ __forceinline__ void mma_panel(const char GK_LDS* st, float16v (&acc)[T::TM][T::TN],
+__device__ __forceinline__ void mma_panel(const char GK_LDS* st, typename T::Acc (&acc)[T::TM][T::TN],
                                           const LaneOffsets<T>& o) {
 #pragma unroll
-  for (int kk = 0; kk < T::BK / 16; ++kk) {
+  for (int kk = 0; kk < T::BK / T::KD; ++kk) {
     Frag<T> f;
     read_frags<T>(f, st, o, kk);
     mfma_step<T>(acc, f);
@@ -307,13 +353,13 @@ __device__ __forceinline__ void mma_panel(const char GK_LDS* st, float16v (&acc)
 // element; row steps are scalar offsets and 32-column steps immediates.
 // ---------------------------------------------------------------------------------------
 template <class T>
-__device__ __forceinline__ void store_tile(const Args& p, const float16v (&acc)[T::TM][T::TN],
+__device__ __forceinline__ void store_tile(const Args& p, const typename T::Acc (&acc)[T::TM][T::TN],
                                            int m0, int n0, int wm, int wn, int lane) {
   const int64_t c0 = (int64_t)m0 * p.ldc + n0;
   const int64_t extC = (int64_t)(p.M - 1) * p.ldc + p.N;
   const __amdgpu_buffer_rsrc_t rc = make_rsrc(p.C + c0, 2 * (extC - c0));
-  const int col = wn * T::WTN + (lane & 31);
-  const int row = wm * T::WTM + (lane >> 5) * 4;
+  const int col = wn * T::WTN + (lane & (T::XB - 1));
+  const int row = wm * T::WTM + (lane / T::XB) * 4;
   const uint32_t vbase = 2u * ((uint32_t)row * (uint32_t)p.ldc + (uint32_t)col);
   const uint32_t ldc2 = 2u * (uint32_t)p.ldc;
   const int ncols = p.N - n0;   // columns of this tile that exist
@@ -321,16 +367,16 @@ __device__ __forceinline__ void store_tile(const Args& p, const float16v (&acc)[
   auto block = [&](auto all_rows) __attribute__((always_inline)) {
 #pragma unroll
     for (int tn = 0; tn < T::TN; ++tn) {
-      if (col + tn * 32 < ncols) {
+      if (col + tn * T::XB < ncols) {
 #pragma unroll
         for (int tm = 0; tm < T::TM; ++tm) {
 #pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int r = tm * 32 + (v >> 2) * 8 + (v & 3);
+          for (int v = 0; v < T::VN; ++v) {
+            const int r = T::M16 ? tm * 16 + v : tm * 32 + (v >> 2) * 8 + (v & 3);
             if (decltype(all_rows)::value || row + r < nrows) {
               const _Float16 h = (_Float16)acc[tm][tn][v];
               __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, h), rc,
-                                                    vbase + tn * 64, (uint32_t)r * ldc2, 0);
+                                                    vbase + tn * T::XB * 2, (uint32_t)r * ldc2, 0);
             }
           }
         }
@@ -347,29 +393,29 @@ __device__ __forceinline__ void store_tile(const Args& p, const float16v (&acc)[
 // lane layout and masks as store_tile; the slice's M x N block starts at `w`).
 template <class T>
 __device__ __forceinline__ void store_partial(const Args& p, float* w,
-                                             const float16v (&acc)[T::TM][T::TN], int m0,
+                                             const typename T::Acc (&acc)[T::TM][T::TN], int m0,
                                              int n0, int wm, int wn, int lane) {
   const int64_t w0 = (int64_t)m0 * p.ldw + n0;
   const int64_t extW = (int64_t)(p.M - 1) * p.ldw + p.N;
   const __amdgpu_buffer_rsrc_t rw = make_rsrc(w + w0, 4 * (extW - w0));
-  const int col = wn * T::WTN + (lane & 31);
-  const int row = wm * T::WTM + (lane >> 5) * 4;
+  const int col = wn * T::WTN + (lane & (T::XB - 1));
+  const int row = wm * T::WTM + (lane / T::XB) * 4;
   const uint32_t vbase = 4u * ((uint32_t)row * (uint32_t)p.ldw + (uint32_t)col);
   const uint32_t ldw4 = 4u * (uint32_t)p.ldw;
   const int ncols = p.N - n0, nrows = p.M - m0;
 #pragma unroll
   for (int tn = 0; tn < T::TN; ++tn) {
-    if (col + tn * 32 < ncols) {
+    if (col + tn * T::XB < ncols) {
 #pragma unroll
       for (int tm = 0; tm < T::TM; ++tm) {
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int r = tm * 32 + (v >> 2) * 8 + (v & 3);
+        for (int v = 0; v < T::VN; ++v) {
+          const int r = T::M16 ? tm * 16 + v : tm * 32 + (v >> 2) * 8 + (v & 3);
           // the element by value first: a bit_cast of the subscript itself reads element 0
           const float x = acc[tm][tn][v];
           if (row + r < nrows)
             __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, x), rw,
-                                                  vbase + tn * 128, (uint32_t)r * ldw4, 0);
+                                                  vbase + tn * T::XB * 4, (uint32_t)r * ldw4, 0);
         }
       }
     }
@@ -572,7 +618,7 @@ __device__ __forceinline__ void dma_tile(const Args& p, int m0, int n0,
   using T = Tile<BM, BN, BK, AKM, BKM, WM, WN>;
   using OA = typename T::OA;
   using OB = typename T::OB;
-  constexpr int KS = BK / 16;              // k steps per panel
+  constexpr int KS = BK / T::KD;           // k steps per panel
   constexpr int NM = T::TM * T::TN;        // MFMAs per k step
   constexpr int ND = OA::READS + OB::READS;  // LDS reads per k step
   constexpr int NV = T::A_LD + T::B_LD;    // buffer->LDS loads per panel
@@ -641,12 +687,12 @@ __device__ __forceinline__ void dma_tile(const Args& p, int m0, int n0,
     head_store<OB>(vb, base + T::A_BYTES, w, lane);
   };
 
-  float16v acc[T::TM][T::TN];
+  typename T::Acc acc[T::TM][T::TN];
 #pragma unroll
   for (int tm = 0; tm < T::TM; ++tm)
 #pragma unroll
     for (int tn = 0; tn < T::TN; ++tn)
-      acc[tm][tn] = float16v{};
+      acc[tm][tn] = typename T::Acc{};
 
   const LaneOffsets<T> lo = lane_offsets<T>(wm, wn, lane);
   // Operands are read RD k steps ahead of the MFMAs that use them: a ring of RD + 1
@@ -679,21 +725,70 @@ __device__ __forceinline__ void dma_tile(const Args& p, int m0, int n0,
       if constexpr (kSplitRefill) {
         // the rest of panel s+1's refill, started at the previous panel's barrier (panel 1 was
         // loaded whole before the loop)
-        if (kk == 0 && s > 0) issue(s + 1, nxt, 2);
+        if (!T::M16 && kk == 0 && s > 0) issue(s + 1, nxt, 2);
       }
       if (kk == KS - RD) {
         wait_vmcnt<(NS - 2) * NV>();   // panel s+1 has landed (this wave's part)
         if (has_last && s + 2 == np) patch(nxt);   // panel s+1 is the last one
         lds_barrier();                 // ... every wave's part
-        if constexpr (NS == 2) issue(s + NS, cur, kSplitRefill ? 1 : 0);
+        if constexpr (NS == 2 && !T::M16) issue(s + NS, cur, kSplitRefill ? 1 : 0);
       }
       const int ka = kk + RD;
-      if (ka < KS)
-        read_frags<T>(f[(j * KS + ka) % (RD + 1)], cur, lo, ka);
-      else
-        read_frags<T>(f[(j * KS + ka) % (RD + 1)], nxt, lo, ka - KS);
-      mfma_step<T>(acc, f[(j * KS + kk) % (RD + 1)]);
-      if constexpr (NS >= 3) {
+      if constexpr (T::M16) {
+        // Scheduled by hand (the MFMAs are asm, which the scheduling hints do not see): one
+        // operand read of the next k step, and at most one refill load, after every fourth of
+        // the step's 64 MFMAs.
+        const char GK_LDS* src = ka < KS ? cur : nxt;
+        const int kr = ka < KS ? ka : ka - KS;
+        Frag<T>& nf = f[(j * KS + ka) % (RD + 1)];
+        const Frag<T>& cf = f[(j * KS + kk) % (RD + 1)];
+        // refill loads of this step: at the barrier step slots [0, A_LD + B_LD/2) of panel
+        // s+2 into `cur`; at the first step the other half of B's slots of panel s+1 (into nxt)
+        const bool bar = kk == KS - RD, spl = kSplitRefill && kk == 0 && s > 0;
+        const int sp = bar ? s + NS : s + 1;
+        const bool live = sp < np;
+        const int64_t k0 = (int64_t)kofs + (int64_t)sp * BK;
+        const int64_t eA = elem_off<OA::KM>(m0, k0, p.lda), eB = elem_off<OB::KM>(n0, k0, p.ldb);
+        const __amdgpu_buffer_rsrc_t rA = make_rsrc(p.A + (live ? eA : 0), live ? 2 * (extA - eA) : 0);
+        const __amdgpu_buffer_rsrc_t rB = make_rsrc(p.B + (live ? eB : 0), live ? 2 * (extB - eB) : 0);
+        char GK_LDS* dA = bar ? cur : nxt;
+        char GK_LDS* dB = dA + T::A_BYTES;
+#pragma unroll
+        for (int i = 0; i < T::TM * T::TN; ++i) {
+          if (i % 4 == 2) {
+            const int q = i / 4;
+            if (bar) {
+              if (q < T::A_LD)
+                buffer_load_lds16(rA, (void GK_LDS*)(dA + (q * OA::NW + w) * 1024), offA[q]);
+              else if (q < T::A_LD + kBHalf)
+                buffer_load_lds16(rB, (void GK_LDS*)(dB + ((q - T::A_LD) * OB::NW + w) * 1024),
+                                  offB[q - T::A_LD]);
+            } else if (spl) {
+              if (q < T::B_LD - kBHalf)
+                buffer_load_lds16(rB, (void GK_LDS*)(dB + ((kBHalf + q) * OB::NW + w) * 1024),
+                                  offB[kBHalf + q]);
+            }
+          }
+          const int tm = i / T::TN, tn = i % T::TN;
+          mfma16(acc[tm][tn], cf.a[tm], cf.b[tn]);
+          if (i % 4 == 0 && i / 4 < T::TM + T::TN) {
+            const int r = i / 4;
+            if (r < T::TM)
+              nf.a[r] = read_operand<typename T::OA>(src, lo.a, r, kr);
+            else
+              nf.b[r - T::TM] = read_operand<typename T::OB>(src, lo.b, r - T::TM, kr);
+          }
+        }
+      } else {
+        if (ka < KS)
+          read_frags<T>(f[(j * KS + ka) % (RD + 1)], cur, lo, ka);
+        else
+          read_frags<T>(f[(j * KS + ka) % (RD + 1)], nxt, lo, ka - KS);
+        mfma_step<T>(acc, f[(j * KS + kk) % (RD + 1)]);
+      }
+      if constexpr (T::M16) {
+        // scheduled above
+      } else if constexpr (NS >= 3) {
         if (kk == 0)
           sched_step<NM, ND, NV>();
         else
@@ -738,6 +833,7 @@ __device__ __forceinline__ void dma_tile(const Args& p, int m0, int n0,
   // The last refills (of panels past the end) must land before the workgroup's LDS is freed
   // (or reused for another tile).
   wait_vmcnt<0>();
+  if constexpr (T::M16) mfma16_drain();
   if constexpr (SPLIT)
     store_partial<T>(p, ws, acc, m0, n0, wm, wn, lane);
   else
@@ -933,12 +1029,12 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_generic(Args p) {
   };
 
   const LaneOffsets<T> lo = lane_offsets<T>(wm, wn, lane);
-  float16v acc[T::TM][T::TN];
+  typename T::Acc acc[T::TM][T::TN];
 #pragma unroll
   for (int tm = 0; tm < T::TM; ++tm)
 #pragma unroll
     for (int tn = 0; tn < T::TN; ++tn)
-      acc[tm][tn] = float16v{};
+      acc[tm][tn] = typename T::Acc{};
 
   if (nk > 0) {
     fetch(0);
@@ -950,6 +1046,7 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_generic(Args p) {
     mma_panel<T>((const char GK_LDS*)smem + (s & 1) * T::STAGE, acc, lo);
     if (s + 1 < nk) deposit((s + 1) & 1);
   }
+  if constexpr (T::M16) mfma16_drain();
   store_tile<T>(p, acc, m0, n0, wm, wn, lane);
 }
 
