@@ -72,13 +72,14 @@ enum {
 };
 
 /* Tile configurations: BM x BN x BK, computed by a workgroup of wavefronts (64 lanes each)
- * that each accumulate a block of C with 32x32x16 fp16 MFMAs.  Unless noted, 4 wavefronts in
- * a 2 x 2 arrangement (256 threads).  BK is the k depth of one LDS-staged panel of the DMA
- * path; the generic path stages 64-deep panels for every tile.  Every tile gives the same
- * result bit for bit (each element's k-sum is the same sequence of MFMA steps). */
+ * that each accumulate a block of C with 32x32x16 fp16 MFMAs (tile 1: 16x16x32).  Unless
+ * noted, 4 wavefronts in a 2 x 2 arrangement (256 threads).  BK is the k depth of one
+ * LDS-staged panel of the DMA path; the generic path stages 64-deep panels for every tile.
+ * Every tile gives the same result bit for bit (each element's k-sum is the same sequence of
+ * 16-deep MFMA steps; a 32-deep 16x16x32 step sums exactly as two of them). */
 enum {
     GEMM_F16F32_TILE_AUTO = 0,
-    GEMM_F16F32_TILE_256x256x64 = 1,     /* 2 LDS stages */
+    GEMM_F16F32_TILE_256x256x64 = 1,     /* 2 LDS stages, 16x16x32 MFMAs */
     GEMM_F16F32_TILE_128x128x64 = 2,     /* 2 stages, operands read 3 k steps ahead */
     GEMM_F16F32_TILE_128x64x64 = 3,      /* 2 stages */
     GEMM_F16F32_TILE_256x128x64 = 4,     /* 2 stages, operands read 3 k steps ahead */
