@@ -25,7 +25,7 @@ _lib = None
 def build() -> str:
     """Compile oracle.c into liboracle.so (always recompiles).  Returns the path."""
     tmp = _SO + ".tmp"
-    cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-ffp-contract=off", "-Wall", "-Wextra",
+    cmd = ["gcc", "-O3", "-std=c11", "-fopenmp", "-ffp-contract=off", "-Wall", "-Wextra",
            "-shared", "-fPIC", _SRC, "-o", tmp, "-lm"]
     subprocess.run(cmd, check=True)
     os.replace(tmp, _SO)
@@ -47,6 +47,8 @@ def lib() -> ctypes.CDLL:
         L.oracle_f64_to_f16.restype = ctypes.c_uint16
         L.oracle_gemm.argtypes = [i64, i64, i64, u16p, i64, u16p, i64, u16p, i64]
         L.oracle_gemm.restype = None
+        L.oracle_gemm_plain.argtypes = [i64, i64, i64, u16p, i64, u16p, i64, u16p, i64]
+        L.oracle_gemm_plain.restype = None
         L.oracle_gemm_sampled.argtypes = [i64, u16p, i64, u16p, i64, i64, i64p, i64p, u16p,
                                           ctypes.c_void_p]
         L.oracle_gemm_sampled.restype = None
@@ -97,11 +99,14 @@ def f16_decode_all() -> np.ndarray:
     return np.array([L.oracle_f16_to_f64(h) for h in range(65536)], dtype=np.float64)
 
 
-def gemm(A: np.ndarray, B: np.ndarray, C: np.ndarray | None = None, M=None, N=None, K=None):
+def gemm(A: np.ndarray, B: np.ndarray, C: np.ndarray | None = None, M=None, N=None, K=None,
+         plain: bool = False):
     """C = fp16(sum_k A[i,k] B[k,j]) for 2-D uint16 arrays (row-major, unit inner stride).
 
     M, N, K default to the array shapes; A and B may be wider (their leading dimensions are
     taken from their strides).  If C is given, only its top-left M x N block is written.
+    plain=True runs the one-dot-per-element form instead of the blocked one (same values:
+    both add each element's products in ascending k).
     """
     assert A.dtype == np.uint16 and B.dtype == np.uint16
     M = A.shape[0] if M is None else M
@@ -111,7 +116,8 @@ def gemm(A: np.ndarray, B: np.ndarray, C: np.ndarray | None = None, M=None, N=No
     if C is None:
         C = np.zeros((M, N), dtype=np.uint16)
     assert C.dtype == np.uint16 and C.shape[0] >= M and C.shape[1] >= N
-    lib().oracle_gemm(M, N, K, _ptr(A), _ld(A), _ptr(B), _ld(B), _ptr(C), _ld(C))
+    fn = lib().oracle_gemm_plain if plain else lib().oracle_gemm
+    fn(M, N, K, _ptr(A), _ld(A), _ptr(B), _ld(B), _ptr(C), _ld(C))
     return C
 
 
@@ -150,7 +156,7 @@ def tile_map(num_pid_m: int, num_pid_n: int, group_size_m: int, pid: int):
 
 
 def tile_map_detail(num_pid_m: int, num_pid_n: int, group_size_m: int, pid: int) -> dict:
-    """The notebook's intermediate quantities for program `pid`."""
+    """The notebook's intermediate quantities for program `pid` (from the oracle's walk)."""
     out = np.zeros(6, dtype=np.int64)
     if lib().oracle_tile_map_detail(num_pid_m, num_pid_n, group_size_m, pid, _ptr(out)) != 0:
         raise ValueError("tile_map_detail: argument out of range")

@@ -162,3 +162,48 @@ def test_sampled_matches_full():
     got, s = oracle.gemm_sampled(A, B, r, c, want_f64=True)
     assert np.array_equal(got, C[r, c])
     assert np.array_equal(f16(s), got)
+
+
+# ---------------------------------------------------------------------------------------
+# The blocked form (64 x 256 blocks of C, k outermost inside a block) on shapes that span
+# several blocks and end in partial ones.
+# ---------------------------------------------------------------------------------------
+def test_multi_block_matches_numpy_blas_when_sums_are_exact():
+    """Across block edges (rows 64, 128, columns 256, 512 and ragged last blocks) the result
+    is the one numpy's float64 product gives when every sum is exact in fp64."""
+    A, B = operands(150, 600, 300, "u(-0.5,0.5)", 31)
+    assert np.array_equal(oracle.gemm(A, B), f16(as_f64(A) @ as_f64(B)))
+    A, B = operands(65, 257, 129, "u(0,1)", 32)
+    assert np.array_equal(oracle.gemm(A, B), f16(as_f64(A) @ as_f64(B)))
+
+
+def test_multi_block_identity_and_one_hot():
+    rng = np.random.default_rng(33)
+    B = random_f16(rng, (300, 530), -20, 10)
+    assert np.array_equal(oracle.gemm(f16(np.eye(300)), B), B)
+    A = np.zeros((130, 300), dtype=np.uint16)
+    A[:, 299] = f16(1.0)
+    assert np.array_equal(oracle.gemm(A, B), np.broadcast_to(B[299], (130, 530)))
+
+
+@pytest.mark.parametrize("M,N,K", [(130, 520, 77), (65, 257, 300), (1, 700, 40), (200, 3, 90),
+                                   (64, 256, 5), (129, 513, 1)])
+def test_blocked_equals_one_dot_per_element(M, N, K):
+    """Both forms add each element's products in ascending k, so they agree bit for bit --
+    with subnormals, infinities and NaNs among the operands too.  The sign of a NaN result is
+    not part of the definition (the two loops may hand the adder its operands in either
+    order, and x86 keeps the first NaN operand's sign), so NaNs compare as one value."""
+    rng = np.random.default_rng(M * 1000 + N + K)
+    A = random_f16(rng, (M, K), -24, 8)
+    B = random_f16(rng, (K, N), -24, 8)
+    for X, count in ((A, 3), (B, 3)):
+        r = rng.integers(0, X.shape[0], count)
+        c = rng.integers(0, X.shape[1], count)
+        X[r, c] = rng.choice([0x7C00, 0xFC00, 0x7E00], count)
+    def canon(h):
+        h = h.copy()
+        h[((h & 0x7C00) == 0x7C00) & ((h & 0x03FF) != 0)] = 0x7E00
+        return h
+
+    blocked, plain = oracle.gemm(A, B), oracle.gemm(A, B, plain=True)
+    assert np.array_equal(canon(blocked), canon(plain))

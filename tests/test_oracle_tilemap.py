@@ -149,3 +149,28 @@ def test_program_tiles_composition_is_bijection():
             t = oracle.program_tiles(m, n, G, remap)
             assert np.unique(t[:, 0]).size == m * n
             assert np.unique(t[:, 1] * n + t[:, 2]).size == m * n
+
+
+def test_program_tiles_composition_hand_derived():
+    """The XCD permutation is applied to the hardware id first and the grouped map to its
+    result.  Worked by hand from the two definitions:
+      * 8 x 12 tiles, G = 2, remap on: P = 96 = 8 x 12, so each die owns 12 consecutive
+        logical ids; hardware id 1 is die 1's first workgroup -> logical id 12 -> group 0
+        (24 ids), column-major over its 2 rows -> row 12 mod 2 = 0, column 12 // 2 = 6.
+        Applying the map first would give the tile of id 1, (1, 0), instead.
+      * 32 x 32 tiles, G = 8, remap on: die 0 receives hardware ids 0, 8, 16, ... and they
+        become logical ids 0, 1, 2, ...; the first 32 of them fill rows 0-7 of columns 0-3
+        (an 8 x 4 block of tiles), id t at (t mod 8, t // 8).
+      * remap off: logical id = hardware id."""
+    t = oracle.program_tiles(8, 12, 2, True)
+    assert tuple(t[1]) == (12, 0, 6)
+    assert tuple(t[0]) == (0, 0, 0)
+    assert tuple(t[8]) == (1, 1, 0)          # die 0's second workgroup: logical id 1
+    assert tuple(t[95]) == (95, 7, 11)       # die 7's last: 7*12 + 11 = 95
+    t = oracle.program_tiles(32, 32, 8, True)
+    for j in range(32):
+        assert tuple(t[8 * j]) == (j, j % 8, j // 8), j
+    die0 = {(int(r), int(c)) for r, c in t[0:256:8, 1:]}
+    assert die0 == {(r, c) for r in range(8) for c in range(4)}
+    t = oracle.program_tiles(8, 12, 2, False)
+    assert tuple(t[1]) == (1, 1, 0) and tuple(t[60]) == (60, 4, 6)
