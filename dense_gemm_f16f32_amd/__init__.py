@@ -211,22 +211,29 @@ def matmul(a, b, out=None, *, M=None, N=None, K=None, stream=None, workspace=Non
     M = a.shape[0] if M is None else M
     K = a.shape[1] if K is None else K
     N = b.shape[1] if N is None else N
-    if out is None:
-        out = torch.empty((max(M, 0), max(N, 0)), dtype=a.dtype, device=a.device)
     # Negative sizes are left to the library, which returns ERR_DIM for them.
-    for t, rows, cols, what in ((a, M, K, "a"), (b, K, N, "b"), (out, M, N, "out")):
+    for t, rows, cols, what in ((a, M, K, "a"), (b, K, N, "b")) + (
+            () if out is None else ((out, M, N, "out"),)):
         if rows > t.shape[0] or cols > t.shape[1]:
             raise ValueError(f"{what} is {tuple(t.shape)}; the call needs its first "
                              f"{rows} x {cols} block (M={M}, N={N}, K={K})")
-    if not all(t.is_cuda for t in (a, b, out)):
+    if not all(t.is_cuda for t in ((a, b) if out is None else (a, b, out))):
         raise ValueError("operands must be CUDA tensors")
+    # Memory this call allocates belongs to the stream the kernels run on: torch's caching
+    # allocator hands a freed block out again only to work on its own stream, so the
+    # workspace freed on return cannot be reused by other streams while the kernels still use
+    # it.
+    s = torch.cuda.current_stream() if stream is None else stream
+    if out is None:
+        with torch.cuda.stream(s):
+            out = torch.empty((max(M, 0), max(N, 0)), dtype=a.dtype, device=a.device)
     args = (M, N, K, a.data_ptr(), a.stride(0), a.stride(1), b.data_ptr(), b.stride(0),
             b.stride(1), out.data_ptr(), out.stride(0), out.stride(1))
     if workspace is not None and "split_k" not in opts:
         opts = dict(opts, split_k=SPLIT_K_AUTO)
     o = Opts(**opts) if opts else None
     if o is None or o.split_k in (0, 1):
-        rc = gemm_f16f32_strided(*args, _stream_handle(stream), o)
+        rc = gemm_f16f32_strided(*args, s.cuda_stream, o)
         if rc != OK:
             raise GemmError(rc, "gemm_f16f32_strided")
         return out
@@ -235,11 +242,12 @@ def matmul(a, b, out=None, *, M=None, N=None, K=None, stream=None, workspace=Non
         if rc != OK:
             raise GemmError(rc, "gemm_f16f32_strided_plan")
         if info["workspace_bytes"] > 0:
-            workspace = torch.empty(info["workspace_bytes"], dtype=torch.uint8,
-                                    device=out.device)
+            with torch.cuda.stream(s):
+                workspace = torch.empty(info["workspace_bytes"], dtype=torch.uint8,
+                                        device=out.device)
     ptr, nbytes = (0, 0) if workspace is None else (workspace.data_ptr(),
                                                     workspace.numel() * workspace.element_size())
-    rc = gemm_f16f32_strided_ws(*args, ptr, nbytes, _stream_handle(stream), o)
+    rc = gemm_f16f32_strided_ws(*args, ptr, nbytes, s.cuda_stream, o)
     if rc != OK:
         raise GemmError(rc, "gemm_f16f32_strided_ws")
     return out

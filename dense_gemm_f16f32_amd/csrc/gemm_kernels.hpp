@@ -306,17 +306,41 @@ __device__ __forceinline__ void read_frags(Frag<T>& f, const char GK_LDS* st,
 
 // One 16x16x32 MFMA accumulating in place on accumulator registers.  Written as inline asm:
 // through the builtin the compiler copied every 4-register accumulator once per MFMA.  The
-// compiler's hazard checks do not see inside the asm, so the code around it keeps the waits
-// the hardware needs: the accumulators are zeroed well before the first MFMA (a whole panel
-// prologue lies between) and read by the epilogue only after `mfma16_drain`.
+// compiler's hazard checks do not see inside the asm, so the code around it provides the wait
+// states the hardware needs (CDNA3/CDNA4 ISA guides, "Dependency Resolution: Required
+// Independent Instructions"); every asm here is volatile, and volatile asms keep their order:
+//  * VALU or v_accvgpr_write of an accumulator, then an MFMA reading it as SrcC (a few wait
+//    states): `mfma16_pin_zero` pins the zeroed accumulators in place and issues 8 wait
+//    states after them, before any MFMA of the tile.
+//  * MFMA result, then v_accvgpr_read or any other read of it (the longest entry of the
+//    table, for a 16-pass MFMA, is under 20 wait states): `mfma16_drain` issues 32 wait
+//    states after the tile's last MFMA and only then hands the accumulators back to the
+//    compiler, so no read is scheduled above it.
+//  * An LDS load overwriting an MFMA's A or B operand registers while it may still read them:
+//    the operand ring holds two k steps, and a register is reloaded at the earliest 29 MFMAs
+//    after the last MFMA that read it (see `panel` in dma_tile).
+//  * MFMA result fed to the next MFMA on the same accumulator (SrcC = vdst, same size): back
+//    to back is allowed; here 63 other MFMAs lie between.
 __device__ __forceinline__ void mfma16(float4v& acc, const half8& a, const half8& b) {
   asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
 
-// Wait states between the last MFMA written as asm and the first read of its result
-// (4 x 8, more than the longest such dependency of the 16x16x32 instruction).
-__device__ __forceinline__ void mfma16_drain() {
+template <class T>
+__device__ __forceinline__ void mfma16_pin_zero(typename T::Acc (&acc)[T::TM][T::TN]) {
+#pragma unroll
+  for (int tm = 0; tm < T::TM; ++tm)
+#pragma unroll
+    for (int tn = 0; tn < T::TN; ++tn) asm volatile("" : "+a"(acc[tm][tn]));
+  asm volatile("s_nop 7" ::: "memory");
+}
+
+template <class T>
+__device__ __forceinline__ void mfma16_drain(typename T::Acc (&acc)[T::TM][T::TN]) {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+#pragma unroll
+  for (int tm = 0; tm < T::TM; ++tm)
+#pragma unroll
+    for (int tn = 0; tn < T::TN; ++tn) asm volatile("" : "+a"(acc[tm][tn]));
 }
 
 template <class T>
@@ -693,6 +717,7 @@ __device__ __forceinline__ void dma_tile(const Args& p, int m0, int n0,
 #pragma unroll
     for (int tn = 0; tn < T::TN; ++tn)
       acc[tm][tn] = typename T::Acc{};
+  if constexpr (T::M16) mfma16_pin_zero<T>(acc);
 
   const LaneOffsets<T> lo = lane_offsets<T>(wm, wn, lane);
   // Operands are read RD k steps ahead of the MFMAs that use them: a ring of RD + 1
@@ -833,7 +858,7 @@ __device__ __forceinline__ void dma_tile(const Args& p, int m0, int n0,
   // The last refills (of panels past the end) must land before the workgroup's LDS is freed
   // (or reused for another tile).
   wait_vmcnt<0>();
-  if constexpr (T::M16) mfma16_drain();
+  if constexpr (T::M16) mfma16_drain<T>(acc);
   if constexpr (SPLIT)
     store_partial<T>(p, ws, acc, m0, n0, wm, wn, lane);
   else
@@ -1035,6 +1060,7 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_generic(Args p) {
 #pragma unroll
     for (int tn = 0; tn < T::TN; ++tn)
       acc[tm][tn] = typename T::Acc{};
+  if constexpr (T::M16) mfma16_pin_zero<T>(acc);
 
   if (nk > 0) {
     fetch(0);
@@ -1046,7 +1072,7 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_generic(Args p) {
     mma_panel<T>((const char GK_LDS*)smem + (s & 1) * T::STAGE, acc, lo);
     if (s + 1 < nk) deposit((s + 1) & 1);
   }
-  if constexpr (T::M16) mfma16_drain();
+  if constexpr (T::M16) mfma16_drain<T>(acc);
   store_tile<T>(p, acc, m0, n0, wm, wn, lane);
 }
 

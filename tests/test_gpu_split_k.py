@@ -224,3 +224,26 @@ def test_automatic_split_matches_its_explicit_choice():
                                dict(split_k=g.SPLIT_K_AUTO))
     assert rc == g.OK
     assert np.array_equal(from_dev(Cv), unsplit)
+
+
+def test_matmul_on_a_side_stream_keeps_its_workspace():
+    """matmul(stream=side) with split K and no workspace: the workspace (and `out`) are
+    allocated on the side stream, so memory the current stream allocates and writes right
+    after the call -- while the side stream's kernels may still run -- is never the
+    workspace.  The result must equal the same call on the current stream."""
+    M, N, K = 128, 128, 8192
+    A, B = operands(M, N, K, "u(-0.5,0.5)", 77)
+    Ad, Bd = to_dev(A), to_dev(B)
+    want = from_dev(g.matmul(Ad, Bd, split_k=8))
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    for rep in range(3):
+        C = g.matmul(Ad, Bd, split_k=8, stream=side)
+        junk = [torch.full((1 << 20,), 0x7E00 + rep, dtype=torch.int16, device="cuda")
+                for _ in range(8)]
+        torch.cuda.current_stream().wait_stream(side)
+        got = from_dev(C)
+        assert np.array_equal(got, want), rep
+        del junk
+    assert_within_tolerance(want, oracle.gemm(A, B), "split K on a side stream")
