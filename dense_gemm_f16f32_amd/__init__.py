@@ -1,8 +1,8 @@
 """Python binding of libgemm_f16f32.so (the gfx950 fp16/fp32-accumulate GEMM).
 
 The functions named like the C-ABI (gemm_f16f32, gemm_f16f32_ex, gemm_f16f32_plan,
-gemm_f16f32_strided, gemm_f16f32_strided_ws, gemm_f16f32_strided_plan, gemm_f16f32_tile_map,
-gemm_f16f32_strerror, gemm_f16f32_version) only marshal arguments into the library; every step
+gemm_f16f32_strided, gemm_f16f32_strided_ws, gemm_f16f32_strided_scratch,
+gemm_f16f32_strided_plan, gemm_f16f32_tile_map, gemm_f16f32_strerror, gemm_f16f32_version) only marshal arguments into the library; every step
 of the computation runs in its HIP kernels.  `matmul` is the same call for torch tensors: it
 passes their device pointers, element strides (row- or column-major, any leading dimension)
 and torch's current HIP stream, and for split K a workspace tensor.  PyTorch is used for
@@ -21,7 +21,8 @@ LIB_PATH = os.path.join(PKG, "libgemm_f16f32.so")
 
 OK = 0
 (ERR_DIM, ERR_NULL, ERR_LD, ERR_OVERLAP, ERR_OPTS, ERR_TOO_LARGE, ERR_HIP,
- ERR_WORKSPACE) = range(-1, -9, -1)
+ ERR_WORKSPACE, ERR_SCRATCH) = range(-1, -10, -1)
+SCRATCH_BYTES = 16 << 20   # the static split-K scratch of gemm_f16f32_strided_scratch
 (TILE_AUTO, TILE_256x256x64, TILE_128x128x64, TILE_128x64x64, TILE_256x128x64,
  TILE_256x256x32, TILE_64x64x32, TILE_128x64x32, TILE_256x256x64_W8, TILE_64x64x64,
  TILE_32x32x64, TILE_32x64x64, TILE_64x32x64, TILE_32x64x128, TILE_64x64x128, TILE_32x32x128,
@@ -94,6 +95,8 @@ def lib() -> ctypes.CDLL:
         L.gemm_f16f32_strided_ws.argtypes = _STRIDED_ARGS + [_vp, _i64, _vp,
                                                              ctypes.POINTER(Opts)]
         L.gemm_f16f32_strided_ws.restype = ctypes.c_int
+        L.gemm_f16f32_strided_scratch.argtypes = _STRIDED_ARGS + [_vp, ctypes.POINTER(Opts)]
+        L.gemm_f16f32_strided_scratch.restype = ctypes.c_int
         L.gemm_f16f32_strided_plan.argtypes = _STRIDED_ARGS + [ctypes.POINTER(Opts),
                                                                ctypes.POINTER(PlanInfo)]
         L.gemm_f16f32_strided_plan.restype = ctypes.c_int
@@ -150,6 +153,14 @@ def gemm_f16f32_strided_ws(M, N, K, A, stride_am, stride_ak, B, stride_bk, strid
                                         stride_bn, C, stride_cm, stride_cn, workspace,
                                         workspace_bytes, stream,
                                         ctypes.byref(o) if o is not None else None)
+
+
+def gemm_f16f32_strided_scratch(M, N, K, A, stride_am, stride_ak, B, stride_bk, stride_bn, C,
+                                stride_cm, stride_cn, stream=None, opts=None) -> int:
+    o = _opts(opts)
+    return lib().gemm_f16f32_strided_scratch(M, N, K, A, stride_am, stride_ak, B, stride_bk,
+                                             stride_bn, C, stride_cm, stride_cn, stream,
+                                             ctypes.byref(o) if o is not None else None)
 
 
 def gemm_f16f32_strided_plan(M, N, K, A, stride_am, stride_ak, B, stride_bk, stride_bn, C,

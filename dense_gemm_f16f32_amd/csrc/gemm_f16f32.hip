@@ -6,13 +6,20 @@
 #include <stdint.h>
 
 #include <cmath>
+#include <mutex>
 
 #include "gemm_kernels.hpp"
 #include "gemm_tiles.hpp"
 
+// Split-K workspace of gemm_f16f32_strided_scratch: one array per GPU, resident from the
+// library's code-object load until the process ends.  In host code `scratch` only names the
+// symbol; its device address comes from hipGetSymbolAddress, once per device, and only that
+// address is ever passed to a kernel.
+static __device__ __align__(256) unsigned char scratch[GEMM_F16F32_SCRATCH_BYTES];
+
 namespace {
 
-constexpr int kVersion = 400;  // 0.4.0
+constexpr int kVersion = 500;  // 0.5.0
 constexpr int kCUs = 256;       // compute units of an MI355X (persistent grid width, split-K grid budget)
 
 struct TileDesc {
@@ -491,6 +498,32 @@ int plan(const Problem& pr, const gemm_f16f32_opts* opts, gemm_f16f32_plan_info*
   return rc;
 }
 
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mutex;
+void* scratch_ptr[kMaxDevices] = {};
+
+// The scratch array's device address on the device `stream` runs on, which must be the
+// current device (looked up with that device current on its first use).
+int scratch_for_stream(hipStream_t stream, void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return GEMM_F16F32_ERR_HIP;
+  if (stream != nullptr) {
+    hipDevice_t sdev = -1;
+    if (hipStreamGetDevice(stream, &sdev) != hipSuccess) return GEMM_F16F32_ERR_HIP;
+    if (sdev != dev) return GEMM_F16F32_ERR_SCRATCH;
+  }
+  std::lock_guard<std::mutex> lock(scratch_mutex);
+  if (scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+      return GEMM_F16F32_ERR_HIP;
+    scratch_ptr[dev] = p;
+  }
+  *out = scratch_ptr[dev];
+  return GEMM_F16F32_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -533,6 +566,30 @@ int gemm_f16f32_strided_ws(int64_t M, int64_t N, int64_t K, const uint16_t* A,
   return rc != GEMM_F16F32_OK ? rc : run(pr, stream, opts, workspace, workspace_bytes);
 }
 
+int gemm_f16f32_strided_scratch(int64_t M, int64_t N, int64_t K, const uint16_t* A,
+                                int64_t stride_am, int64_t stride_ak, const uint16_t* B,
+                                int64_t stride_bk, int64_t stride_bn, uint16_t* C,
+                                int64_t stride_cm, int64_t stride_cn, void* stream,
+                                const gemm_f16f32_opts* opts) {
+  Problem pr;
+  int rc = strided_problem(M, N, K, A, stride_am, stride_ak, B, stride_bk, stride_bn, C,
+                           stride_cm, stride_cn, &pr);
+  if (rc != GEMM_F16F32_OK) return rc;
+  // An explicit split larger than the array is refused, not silently run unsplit.
+  if (opts != nullptr && opts->split_k >= 2) {
+    Part parts[4];
+    int n = 0;
+    rc = plan_parts(pr, opts, INT64_MAX, parts, &n);
+    if (rc != GEMM_F16F32_OK) return rc;
+    if (n > 0 && parts[0].r.workspace_bytes > GEMM_F16F32_SCRATCH_BYTES)
+      return GEMM_F16F32_ERR_SCRATCH;
+  }
+  void* ws = nullptr;
+  rc = scratch_for_stream((hipStream_t)stream, &ws);
+  if (rc != GEMM_F16F32_OK) return rc;
+  return run(pr, stream, opts, ws, GEMM_F16F32_SCRATCH_BYTES);
+}
+
 int gemm_f16f32_strided_plan(int64_t M, int64_t N, int64_t K, const uint16_t* A,
                              int64_t stride_am, int64_t stride_ak, const uint16_t* B,
                              int64_t stride_bk, int64_t stride_bn, const uint16_t* C,
@@ -568,6 +625,9 @@ const char* gemm_f16f32_strerror(int code) {
     case GEMM_F16F32_ERR_HIP: return "HIP runtime rejected the launch";
     case GEMM_F16F32_ERR_WORKSPACE:
       return "split K needs a 16-byte aligned workspace of at least plan_info.workspace_bytes";
+    case GEMM_F16F32_ERR_SCRATCH:
+      return "split K needs more than the library's 16 MiB static scratch, or the stream is "
+             "not on the current device";
     default: return "unknown error code";
   }
 }

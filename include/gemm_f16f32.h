@@ -28,7 +28,9 @@
  *
  * Ownership and execution: A, B, C (and the split-K workspace of gemm_f16f32_strided_ws) are
  * device pointers owned by the caller.  The library allocates nothing and keeps no state
- * between calls, so calls from several host threads are safe.  A call checks its arguments,
+ * between calls, so calls from several host threads are safe -- except for
+ * gemm_f16f32_strided_scratch, whose split-K workspace is one static device array per GPU
+ * (see there).  A call checks its arguments,
  * launches on `stream` (a hipStream_t; NULL is the null stream) and returns without waiting;
  * faults inside a kernel surface at the caller's next synchronisation.  Only C[i][j] with i < M, j < N is written (padding between N and ldc is
  * left as it was).  M == 0 or N == 0 is a successful no-op; K == 0 writes +0 to the M x N
@@ -66,9 +68,13 @@ enum {
                                        that fails this gives way to the 32 x 32 x 64 tile
                                        first; a forced tile does not. */
     GEMM_F16F32_ERR_HIP = -7,       /* the HIP runtime rejected the launch */
-    GEMM_F16F32_ERR_WORKSPACE = -8  /* split K planned but no workspace (an entry point without
+    GEMM_F16F32_ERR_WORKSPACE = -8, /* split K planned but no workspace (an entry point without
                                        one), or the workspace is smaller than
                                        plan_info.workspace_bytes or not 16-byte aligned */
+    GEMM_F16F32_ERR_SCRATCH = -9    /* gemm_f16f32_strided_scratch: the split asked for needs
+                                       more than GEMM_F16F32_SCRATCH_BYTES of workspace, or
+                                       `stream` belongs to a device other than the current
+                                       one */
 };
 
 /* Tile configurations: BM x BN x BK, computed by a workgroup of wavefronts (64 lanes each)
@@ -227,6 +233,30 @@ int gemm_f16f32_strided_ws(int64_t M, int64_t N, int64_t K, const uint16_t *A,
                            int64_t stride_bk, int64_t stride_bn, uint16_t *C, int64_t stride_cm,
                            int64_t stride_cn, void *workspace, int64_t workspace_bytes,
                            void *stream, const gemm_f16f32_opts *opts);
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): gemm_f16f32_strided_ws without a workspace
+ * argument.  A split (opts->split_k >= 2, or GEMM_F16F32_SPLIT_K_AUTO) keeps its fp32 slices
+ * in a file-scope device array of GEMM_F16F32_SCRATCH_BYTES (16 MiB) that each GPU the
+ * library runs on holds until the process ends; the call allocates nothing and calls no
+ * allocating routine.  Its device address is looked up once per device, on the first call
+ * made with that device current (hipGetSymbolAddress); `stream` must belong to the current
+ * device (ERR_SCRATCH otherwise; NULL is the current device's null stream).  An explicit
+ * split whose plan needs more than GEMM_F16F32_SCRATCH_BYTES returns ERR_SCRATCH before
+ * anything is launched; the automatic split falls back to no split when it would not fit.
+ * Nothing in the array needs to start at zero: the slice kernel writes every element the
+ * reduction adds into C before the reduction reads it.  Every call on one GPU shares that
+ * GPU's array, so calls that may overlap in time on one GPU (different streams, or different
+ * host threads) race on it and give wrong results; calls ordered on one stream are safe.
+ * Results are those of gemm_f16f32_strided_ws with the same arguments, bit for bit.
+ */
+#define GEMM_F16F32_SCRATCH_BYTES ((int64_t)16 << 20)
+int gemm_f16f32_strided_scratch(int64_t M, int64_t N, int64_t K, const uint16_t *A,
+                                int64_t stride_am, int64_t stride_ak, const uint16_t *B,
+                                int64_t stride_bk, int64_t stride_bn, uint16_t *C,
+                                int64_t stride_cm, int64_t stride_cn, void *stream,
+                                const gemm_f16f32_opts *opts);
 
 /* Host only, no GPU work: what gemm_f16f32_strided (or, with split_k, gemm_f16f32_strided_ws)
  * with these arguments would launch, including the workspace a split needs. */

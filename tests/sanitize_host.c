@@ -45,6 +45,16 @@ int hipLaunchKernel(const void *f, dim3_t g, dim3_t b, void **a, size_t s, void 
     return 1; /* an error code: the library reports GEMM_F16F32_ERR_HIP */
 }
 int hipGetLastError(void) { return 0; }
+void __hipRegisterVar(void **m, void *var, char *hv, const char *dv, int ext, size_t size,
+                      int constant, int global)
+{
+    (void)m, (void)var, (void)hv, (void)dv, (void)ext, (void)size, (void)constant, (void)global;
+}
+/* One fake device, no streams of other devices; the static scratch's "address" is a fake
+ * pointer that is never dereferenced (nothing is launched). */
+int hipGetDevice(int *d) { *d = 0; return 0; }
+int hipStreamGetDevice(void *s, int *d) { (void)s; *d = 0; return 0; }
+int hipGetSymbolAddress(void **p, const void *sym) { (void)sym; *p = (void *)(uintptr_t)0x4000000000ull; return 0; }
 
 static uint64_t state = 0x2545F4914F6CDD1Dull;
 static uint64_t next(void)
@@ -119,15 +129,25 @@ int main(void)
                                           op);
                 (void)gemm_f16f32_strided_ws(M, N, K, A, sam, sak, B, sbk, sbn, C, scm, scn, ws,
                                              wsb, NULL, op);
-                runs += 2;
-            } else if (use_opts && o.split_k >= 2 && info.splits > 1 &&
-                       wsb < info.workspace_bytes) {
+                (void)gemm_f16f32_strided_scratch(M, N, K, A, sam, sak, B, sbk, sbn, C, scm, scn,
+                                                  NULL, op);
+                runs += 3;
+            } else if (use_opts && o.split_k >= 2 && info.splits > 1) {
                 /* an explicit split with too small a workspace is refused before any launch
                    (the automatic choice would run unsplit instead) */
-                if (gemm_f16f32_strided_ws(M, N, K, A, sam, sak, B, sbk, sbn, C, scm, scn, ws,
-                                           wsb, NULL, op) != GEMM_F16F32_ERR_WORKSPACE)
-                    return 1;
-                ++runs;
+                if (wsb < info.workspace_bytes) {
+                    if (gemm_f16f32_strided_ws(M, N, K, A, sam, sak, B, sbk, sbn, C, scm, scn, ws,
+                                               wsb, NULL, op) != GEMM_F16F32_ERR_WORKSPACE)
+                        return 1;
+                    ++runs;
+                }
+                /* likewise one that needs more than the static scratch */
+                if (info.workspace_bytes > GEMM_F16F32_SCRATCH_BYTES) {
+                    if (gemm_f16f32_strided_scratch(M, N, K, A, sam, sak, B, sbk, sbn, C, scm,
+                                                    scn, NULL, op) != GEMM_F16F32_ERR_SCRATCH)
+                        return 1;
+                    ++runs;
+                }
             }
         }
         ++plans;

@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol():
 
 def test_version_and_strerror():
     assert g.gemm_f16f32_version() >= 100
-    for code in [0, -1, -2, -3, -4, -5, -6, -7, -8]:
+    for code in [0, -1, -2, -3, -4, -5, -6, -7, -8, -9]:
         assert g.gemm_f16f32_strerror(code) and g.gemm_f16f32_strerror(code) != "unknown error code"
     assert g.gemm_f16f32_strerror(-99) == "unknown error code"
 
