@@ -181,32 +181,37 @@ __device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t r, void
 #endif
 }
 
-// Swizzles.  The hardware serves a 16-byte-per-lane LDS read 8 lanes (128 B) or 16 lanes
-// (256 B) at a time, so the rows touched by any 8 (and any 16) consecutive lanes must land on
-// distinct bank groups.
+// Swizzles.  How gfx950 serves LDS reads (measured with one-wave probes and the
+// SQ_LDS_BANK_CONFLICT counter): 64 banks of 4 bytes, i.e. a 256-byte bank line of 16
+// 16-byte bank groups.  ds_read_b128 takes 4 cycles of 16 lanes each, and the 16 lanes of a
+// cycle are not consecutive: within each half of the wave (lanes 0-31, 32-63) the 4-lane
+// quads are split by the parity of the quad index (bits 2-4 of the lane), so lanes 0-3,
+// 12-15, 20-23 and 24-27 share a cycle, and so do 4-7, 8-11, 16-19 and 28-31.
+// ds_read_b64_tr_b16 takes 2 cycles, lanes 0-31 and 32-63.  A conflict-free read gives the
+// lanes of each cycle 16 distinct bank groups (32 distinct 8-byte halves for the transposing
+// read).
 //  * k-major, 256-byte rows (BK = 128): every row starts on the same bank, and swz = r mod 16
-//    puts 16 consecutive rows on the 16 distinct 16-byte bank groups of a 256-byte line.
-//  * k-major, 128-byte rows (BK = 64): 32 lanes read 32 consecutive rows at one logical
-//    chunk; swz = (r mod 8) xor bit 3 of r gives 8 rows 8 distinct chunk positions and 16
-//    rows 16 distinct (row parity, position) pairs.
-//  * k-major, 64-byte rows (BK = 32): two rows share a bank line; swz = (bits 1-2 of r) xor
-//    (bits 3-4) gives distinct (r mod 2, position) over 8 rows and distinct (r mod 4,
-//    position) over 16.
-//    Both depend on r mod 32 only, so rows 32 apart (the next 32-row MFMA block) share the
+//    puts 16 consecutive rows on the 16 bank groups.
+//  * k-major, 128-byte rows (BK = 64): two rows per bank line; swz = bits 1-3 of r.  With
+//    32x32x16 MFMAs a cycle reads rows {4q .. 4q+3} for four quads q of one parity at one
+//    chunk; with 16x16x32 MFMAs rows 0-15 at two chunks.  Both land on 16 distinct groups.
+//  * k-major, 64-byte rows (BK = 32): four rows per bank line; swz = bits 2-3 of r.
+//    All three depend on r mod 16, so rows 16 or 32 apart (the next MFMA block) share the
 //    swizzle and their addresses differ by a constant.
-//  * x-major: a transposing read covers 4 consecutive rows x 2 (16 lanes) or x 4 (32 lanes)
-//    consecutive chunks; the XOR values 0, 10, 4, 14 for r % 4 = 0..3 (masked to the row's
-//    chunk count) spread both footprints over distinct banks.  Rows of 4 chunks (64 bytes)
-//    need none: 4 consecutive rows already fill one 256-byte bank line.
+//  * x-major: a transposing read covers 4 consecutive rows x 2 (16 lanes) chunks per 16-lane
+//    group; the XOR values 0, 10, 4, 14 for r % 4 = 0..3 (masked to the row's chunk count)
+//    spread the 32 lanes of a cycle over distinct banks.  With 16x16x32 MFMAs the two groups
+//    of a cycle read rows 8 apart, which an extra XOR of 2 by bit 3 of r separates.  Rows of 4
+//    chunks (64 bytes) need none: 4 consecutive rows already fill one 256-byte bank line.
 template <class O>
 __device__ __forceinline__ int swz(int r) {
   if constexpr (O::KM) {
     if constexpr (O::CH == 16)
       return r & 15;
     else if constexpr (O::CH == 8)
-      return (r & 7) ^ ((r >> 3) & 1);
+      return (r >> 1) & 7;
     else
-      return ((r >> 1) ^ (r >> 3)) & 3;
+      return (r >> 2) & 3;
   } else if constexpr (O::CH == 4) {
     return 0;
   } else {
@@ -388,7 +393,22 @@ __device__ __forceinline__ void store_tile(const Args& p, const typename T::Acc 
   const uint32_t ldc2 = 2u * (uint32_t)p.ldc;
   const int ncols = p.N - n0;   // columns of this tile that exist
   const int nrows = p.M - m0;   // rows of this tile that exist
-  auto block = [&](auto all_rows) __attribute__((always_inline)) {
+  auto store = [&](int tm, int tn, int v) __attribute__((always_inline)) {
+    const int r = T::M16 ? tm * 16 + v : tm * 32 + (v >> 2) * 8 + (v & 3);
+    const _Float16 h = (_Float16)acc[tm][tn][v];
+    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, h), rc,
+                                          vbase + tn * T::XB * 2, (uint32_t)r * ldc2, 0);
+  };
+  if (nrows >= T::BM && ncols >= T::BN) {
+    // Whole tile: row by row of the wave's block, so that the stores completing each
+    // 128-byte line of C follow one another.
+#pragma unroll
+    for (int tm = 0; tm < T::TM; ++tm)
+#pragma unroll
+      for (int v = 0; v < T::VN; ++v)
+#pragma unroll
+        for (int tn = 0; tn < T::TN; ++tn) store(tm, tn, v);
+  } else {
 #pragma unroll
     for (int tn = 0; tn < T::TN; ++tn) {
       if (col + tn * T::XB < ncols) {
@@ -397,20 +417,12 @@ __device__ __forceinline__ void store_tile(const Args& p, const typename T::Acc 
 #pragma unroll
           for (int v = 0; v < T::VN; ++v) {
             const int r = T::M16 ? tm * 16 + v : tm * 32 + (v >> 2) * 8 + (v & 3);
-            if (decltype(all_rows)::value || row + r < nrows) {
-              const _Float16 h = (_Float16)acc[tm][tn][v];
-              __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, h), rc,
-                                                    vbase + tn * T::XB * 2, (uint32_t)r * ldc2, 0);
-            }
+            if (row + r < nrows) store(tm, tn, v);
           }
         }
       }
     }
-  };
-  if (nrows >= T::BM)
-    block(std::true_type{});
-  else
-    block(std::false_type{});
+  }
 }
 
 // Split-K epilogue: the fp32 accumulators of one k slice, unrounded, into the workspace (same
