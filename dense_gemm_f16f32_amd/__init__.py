@@ -26,7 +26,7 @@ SCRATCH_BYTES = 16 << 20   # the static split-K scratch of gemm_f16f32_strided_s
 (TILE_AUTO, TILE_256x256x64, TILE_128x128x64, TILE_128x64x64, TILE_256x128x64,
  TILE_256x256x32, TILE_64x64x32, TILE_128x64x32, TILE_256x256x64_W8, TILE_64x64x64,
  TILE_32x32x64, TILE_32x64x64, TILE_64x32x64, TILE_32x64x128, TILE_64x64x128, TILE_32x32x128,
- TILE_64x32x128) = range(17)
+ TILE_64x32x128, TILE_256x256x32_PP) = range(18)
 # tile id -> (BM, BN, BK, threads)
 TILES = {TILE_256x256x64: (256, 256, 64, 256), TILE_128x128x64: (128, 128, 64, 256),
          TILE_128x64x64: (128, 64, 64, 256), TILE_256x128x64: (256, 128, 64, 256),
@@ -35,7 +35,8 @@ TILES = {TILE_256x256x64: (256, 256, 64, 256), TILE_128x128x64: (128, 128, 64, 2
          TILE_64x64x64: (64, 64, 64, 256), TILE_32x32x64: (32, 32, 64, 64),
          TILE_32x64x64: (32, 64, 64, 128), TILE_64x32x64: (64, 32, 64, 128),
          TILE_32x64x128: (32, 64, 128, 128), TILE_64x64x128: (64, 64, 128, 256),
-         TILE_32x32x128: (32, 32, 128, 64), TILE_64x32x128: (64, 32, 128, 128)}
+         TILE_32x32x128: (32, 32, 128, 64), TILE_64x32x128: (64, 32, 128, 128),
+         TILE_256x256x32_PP: (256, 256, 32, 512)}
 PATH_DMA, PATH_GENERIC = 0, 1
 REMAP_DEFAULT, REMAP_ON, REMAP_OFF = 0, 1, 2
 SPLIT_DEFAULT, SPLIT_ON, SPLIT_OFF = 0, 1, 2

@@ -72,8 +72,9 @@ struct Choice {
 // the heuristic with the tile's default group size.  The table was measured on 16-byte
 // aligned rows; when some rows of an operand are not (an odd leading dimension, a 2-byte
 // aligned start), a 16-byte load of a panel row straddles one more cache line, the fetch
-// takes longer, and two wavefronts per SIMD hide it better: there the 8-wavefront 256 x 256
-// tile replaces the 4-wavefront one (measured 3-7 % faster at 2048-4096, even at 8192).
+// takes longer, and two wavefronts per SIMD hide it better: there the 8-wavefront ping-pong
+// tile replaces the 4-wavefront 256 x 256 one (measured 6 % faster on 4095 x 4097 x 4093 and
+// 9 % on 4096^3 with odd leading dimensions, level at 8192^3).
 Choice choose_tile(int64_t M, int64_t N, int64_t K, bool aligned) {
   const int lm = log2_class(M, 5, 13), ln = log2_class(N, 5, 13), lk = log2_class(K, 6, 13);
   Choice c = {heuristic_tile(M, N), 0};
@@ -82,7 +83,7 @@ Choice choose_tile(int64_t M, int64_t N, int64_t K, bool aligned) {
       c = {e.tile, e.group};
       break;
     }
-  if (!aligned && c.tile == GEMM_F16F32_TILE_256x256x64) c.tile = GEMM_F16F32_TILE_256x256x64_W8;
+  if (!aligned && c.tile == GEMM_F16F32_TILE_256x256x64) c.tile = GEMM_F16F32_TILE_256x256x32_PP;
   return c;
 }
 
@@ -367,16 +368,31 @@ template <int BM, int BN, int BK, int NS, int RD, int WM, int WN, bool AKM, bool
 hipError_t launch_layout(const gemm_f16f32_plan_info& r, const gk::Args& a, bool odd,
                          hipStream_t stream) {
   const dim3 grid(r.grid), block(64 * WM * WN);
-  if (r.splits > 1)
+  if constexpr (RD == 0) {
+    // the ping-pong tile on the DMA path
+    if (r.path == GEMM_F16F32_PATH_DMA) {
+      if (r.splits > 1)
+        hipLaunchKernelGGL((gk::gemm_pp_splitk<AKM, BKM>), grid, block, 0, stream, a);
+      else if (r.persistent)
+        hipLaunchKernelGGL((gk::gemm_pp_persistent<AKM, BKM>), grid, block, 0, stream, a);
+      else
+        hipLaunchKernelGGL((gk::gemm_pp<AKM, BKM>), grid, block, 0, stream, a);
+      return hipGetLastError();
+    }
+  } else if (r.splits > 1) {
     hipLaunchKernelGGL((gk::gemm_dma_splitk<BM, BN, BK, NS, RD, WM, WN, AKM, BKM>), grid, block,
                        0, stream, a);
-  else if (r.path == GEMM_F16F32_PATH_DMA && r.persistent)
+    return hipGetLastError();
+  } else if (r.path == GEMM_F16F32_PATH_DMA && r.persistent) {
     hipLaunchKernelGGL((gk::gemm_dma_persistent<BM, BN, BK, NS, RD, WM, WN, AKM, BKM>), grid,
                        block, 0, stream, a);
-  else if (r.path == GEMM_F16F32_PATH_DMA)
+    return hipGetLastError();
+  } else if (r.path == GEMM_F16F32_PATH_DMA) {
     hipLaunchKernelGGL((gk::gemm_dma<BM, BN, BK, NS, RD, WM, WN, AKM, BKM>), grid, block, 0,
                        stream, a);
-  else if (odd)
+    return hipGetLastError();
+  }
+  if (odd)
     hipLaunchKernelGGL((gk::gemm_generic<BM, BN, true, WM, WN, AKM, BKM>), grid, block, 0,
                        stream, a);
   else

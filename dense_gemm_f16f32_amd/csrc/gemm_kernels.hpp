@@ -120,7 +120,6 @@ struct Opnd {
   static constexpr int NOFF = KM ? BK / KD : T;      // per-lane LDS read offsets
   static constexpr int READS = KM ? T : 2 * T;       // LDS read instructions per k step
   static_assert(T >= 1 && LD >= 1 && WX % XB == 0, "operand tile too small for its waves");
-  static_assert(XB == 32 || !KM || CH >= 8, "16-row blocks keep the k-major swizzle");
   static_assert(!KM || CH == 16 || CH == 8 || CH == 4, "k-major LDS rows hold 128-32 halves");
   static_assert(KM || CH == 4 || CH == 8 || CH == 16 || CH == 32,
                 "x-major LDS rows hold 32-256 halves");
@@ -195,7 +194,8 @@ __device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t r, void
 //  * k-major, 128-byte rows (BK = 64): two rows per bank line; swz = bits 1-3 of r.  With
 //    32x32x16 MFMAs a cycle reads rows {4q .. 4q+3} for four quads q of one parity at one
 //    chunk; with 16x16x32 MFMAs rows 0-15 at two chunks.  Both land on 16 distinct groups.
-//  * k-major, 64-byte rows (BK = 32): four rows per bank line; swz = bits 2-3 of r.
+//  * k-major, 64-byte rows (BK = 32): four rows per bank line; swz = (b2, b2 xor b3) from
+//    bits 2 and 3 of r, which serves both MFMA layouts.
 //    All three depend on r mod 16, so rows 16 or 32 apart (the next MFMA block) share the
 //    swizzle and their addresses differ by a constant.
 //  * x-major: a transposing read covers 4 consecutive rows x 2 (16 lanes) chunks per 16-lane
@@ -211,7 +211,7 @@ __device__ __forceinline__ int swz(int r) {
     else if constexpr (O::CH == 8)
       return (r >> 1) & 7;
     else
-      return (r >> 2) & 3;
+      return ((r >> 2) & 1) | ((((r >> 2) ^ (r >> 3)) & 1) << 1);
   } else if constexpr (O::CH == 4) {
     return 0;
   } else {
@@ -926,6 +926,197 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_dma_splitk(Args p) {
   const int p0 = z == 0 ? 0 : p1 - p.panels_per_split;
   dma_tile<BM, BN, BK, NS, RD, WM, WN, AKM, BKM, true>(
       p, pid_m * BM, pid_n * BN, S, p0, p1, p.W + (int64_t)z * p.M * p.ldw);
+}
+
+// ---------------------------------------------------------------------------------------
+// Ping-pong schedule of the 256 x 256 x 32 tile: 8 wavefronts, two per SIMD (the hardware
+// deals a workgroup's waves to the 4 SIMDs in order, so waves w and w + 4 share one).  Each
+// wave owns a 128 x 64 block of C (16x16x32 MFMAs, 8 x 4 accumulator blocks) and holds the
+// operands of one 32-deep panel in registers.  Every wave runs the same sequence per panel
+// u -- fetch (its operands of panel u from LDS, and its share of the DMA refill), barrier,
+// multiply (32 MFMAs back to back), barrier -- but waves 4-7 start one barrier later, so the
+// two waves of a SIMD take turns: in every phase one of them multiplies while the other
+// fetches, and the matrix core always has one wave's uninterrupted run of MFMAs to work on.
+//
+// Panels live in 4 LDS stages (panel u in stage u mod 4).  With waves 0-3 fetching panel u
+// in phase 2u and waves 4-7 in phase 2u+1, panel u-1 was last read in phase 2u-1, so while
+// fetching panel u every wave refills that stage with its share (4 loads) of panel u+3.
+// At the end of its fetch of panel u a wave waits for its share of panel u+1 (the loads of
+// u+2 and u+3 may stay in flight), four phases after issuing it; the next barrier then
+// precedes the first read of panel u+1.  Loads of panels past the end get empty buffer
+// resources (zeros, no memory traffic) so that every wave always has the same loads in
+// flight.  The k order of every element's sum is the same sequence of 32-deep MFMA steps as
+// in the other schedules, so the results are the same bits.
+// ---------------------------------------------------------------------------------------
+struct PPTile {   // one wave's block, in the terms store_tile uses
+  static constexpr int BM = 256, BN = 256, BK = 32, WM = 2, WN = 4;
+  static constexpr int WTM = 128, WTN = 64, XB = 16, KD = 32, TM = 8, TN = 4, VN = 4;
+  static constexpr bool M16 = true;
+  using Acc = float4v;
+};
+
+template <bool AKM, bool BKM, bool SPLIT = false>
+__device__ __forceinline__ void pp_tile(const Args& p, int m0, int n0,
+                                        char GK_LDS* const (&S)[kMaxStages], int p0 = 0,
+                                        int p1 = 0, float* ws = nullptr) {
+  using T = PPTile;
+  using OA = Opnd<256, 32, AKM, 2, 8, 16>;   // operand reads: 2 waves along M
+  using OB = Opnd<256, 32, BKM, 4, 8, 16>;   // operand reads: 4 waves along N
+  constexpr int BK = 32, NS = 4, TM = T::TM, TN = T::TN;
+  constexpr int A_BYTES = OA::BYTES;
+  constexpr int NL = OA::LD + OB::LD;          // loads per wave per panel
+  static_assert(OA::T == TM && OB::T == TN && OA::KD == BK && NL == 4, "ping-pong tile shape");
+
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = w & 1, wn = w >> 1;
+
+  uint32_t offA[OA::LD], offB[OB::LD];
+  slot_offsets<OA>(offA, w, lane, p.lda);
+  slot_offsets<OB>(offB, w, lane, p.ldb);
+  const int64_t extA = extent<AKM>(p.M, p.K, p.lda);
+  const int64_t extB = extent<BKM>(p.N, p.K, p.ldb);
+  const int rk0 = p.K % BK;                     // depth of the head panel (0: none)
+  const int np_all = p.K / BK + (rk0 ? 1 : 0);  // panels of the whole k range
+  // Split K: this call's panels are [p0, p1) of the whole sequence, renumbered from 0 (as in
+  // dma_tile); only the slice holding panel 0 has the head, only the last one patches.
+  const int np = SPLIT ? p1 - p0 : np_all;
+  const int rk = SPLIT && p0 != 0 ? 0 : rk0;
+  const bool has_last = !SPLIT || p1 == np_all;
+  // panel u covers k in [kofs + u BK, + BK)
+  const int kofs = (rk0 ? rk0 - BK : 0) + (SPLIT ? p0 * BK : 0);
+
+  // the last element of each operand, rewritten by the thread whose load slot holds it
+  uint16_t last_a = 0, last_b = 0;
+  const int patch_a = last_element_slot<OA>(m0, p.M, p.K, p.A, extA, tid, last_a);
+  const int patch_b = last_element_slot<OB>(n0, p.N, p.K, p.B, extB, tid, last_b);
+  auto patch = [&](char GK_LDS* base) __attribute__((always_inline)) {
+    if (!has_last) return;
+    if (patch_a >= 0) *(uint16_t GK_LDS*)(base + patch_a) = last_a;
+    if (patch_b >= 0) *(uint16_t GK_LDS*)(base + A_BYTES + patch_b) = last_b;
+  };
+  // This wave's share of full panel u (k0 >= 0); panels past the end load zeros.
+  auto issue = [&](int u, char GK_LDS* base) __attribute__((always_inline)) {
+    const bool live = u < np;
+    const int64_t k0 = (int64_t)kofs + (int64_t)u * BK;
+    dma_panel<OA>(p.A, p.lda, extA, m0, k0, live, offA, base, w);
+    dma_panel<OB>(p.B, p.ldb, extB, n0, k0, live, offB, base + A_BYTES, w);
+  };
+  auto head = [&](char GK_LDS* base) __attribute__((always_inline)) {
+    u32x4 va[OA::LD], vb[OB::LD];
+    head_load<OA>(va, p.A, p.lda, extA, m0, kofs, w, lane);
+    head_load<OB>(vb, p.B, p.ldb, extB, n0, kofs, w, lane);
+    head_store<OA>(va, base, w, lane);
+    head_store<OB>(vb, base + A_BYTES, w, lane);
+  };
+
+  int oa[OA::NOFF], ob[OB::NOFF];
+  operand_offsets<OA>(oa, wm, lane, 0);
+  operand_offsets<OB>(ob, wn, lane, A_BYTES);
+  half8 ra[TM], rb[TN];
+  auto fetch = [&](const char GK_LDS* st) __attribute__((always_inline)) {
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm) ra[tm] = read_operand<OA>(st, oa, tm, 0);
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn) rb[tn] = read_operand<OB>(st, ob, tn, 0);
+  };
+
+  // Prologue: panels 0, 1 and 2 (the head through registers), then panel 0 has landed.
+  if (np > 0) {
+    if (rk)
+      head(S[0]);
+    else
+      issue(0, S[0]);
+    issue(1, S[1]);
+    issue(2, S[2]);
+    wait_vmcnt<2 * NL>();
+    if (np == 1) patch(S[0]);
+  }
+
+  typename T::Acc acc[TM][TN];
+#pragma unroll
+  for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn) acc[tm][tn] = typename T::Acc{};
+  mfma16_pin_zero<T>(acc);
+
+  auto multiply = [&]() __attribute__((always_inline)) {
+    // the operand registers were written by LDS reads before the phase's barrier; a few
+    // wait states more cover any register copy the compiler placed after them.  While it
+    // multiplies, the wave has the higher issue priority on its SIMD.
+    asm volatile("s_setprio 1\n\ts_nop 4" ::: "memory");
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn) mfma16(acc[tm][tn], ra[tm], rb[tn]);
+    asm volatile("s_setprio 0" ::: "memory");
+  };
+  // Panel u from stage j = u mod 4.
+  auto panel = [&](int u, int j) __attribute__((always_inline)) {
+    fetch(S[j]);
+    issue(u + 3, S[(j + 3) % NS]);     // panel u-1's stage, read by every wave by now
+    wait_vmcnt<2 * NL>();              // this wave's share of panel u+1 has landed
+    if (u + 2 == np) patch(S[(j + 1) % NS]);   // panel u+1 is the last one
+    lds_barrier();
+    multiply();
+    lds_barrier();
+  };
+  if (np > 0) {
+    lds_barrier();                     // panel 0 has landed
+    if (w >= 4) lds_barrier();         // waves 4-7 run one phase behind
+    for (int u = 0; u < np; u += NS) {
+#pragma unroll
+      for (int j = 0; j < NS; ++j)
+        if (u + j < np) panel(u + j, j);
+    }
+    if (w < 4) lds_barrier();          // the same number of barriers in every wave
+  }
+  wait_vmcnt<0>();                     // the empty loads past the end, before LDS is freed
+  mfma16_drain<T>(acc);
+  if constexpr (SPLIT)
+    store_partial<T>(p, ws, acc, m0, n0, wm, wn, lane);
+  else
+    store_tile<T>(p, acc, m0, n0, wm, wn, lane);
+}
+
+template <bool AKM, bool BKM>
+__global__ void __launch_bounds__(512) gemm_pp(Args p) {
+  GK_DECLARE_STAGES(4, 32768)
+  int pid, pid_m, pid_n;
+  program_tile(blockIdx.x, p.num_programs, p.num_pid_m, p.num_pid_n, p.group_m, p.xcd_remap,
+               pid, pid_m, pid_n);
+  pp_tile<AKM, BKM>(p, pid_m * 256, pid_n * 256, S);
+}
+
+// The persistent grouped schedule (see gemm_dma_persistent) on the ping-pong tile.
+template <bool AKM, bool BKM>
+__global__ void __launch_bounds__(512) gemm_pp_persistent(Args p) {
+  GK_DECLARE_STAGES(4, 32768)
+  for (int v = blockIdx.x; v < p.num_programs; v += gridDim.x) {
+    int pid, pid_m, pid_n;
+    program_tile(v, p.num_programs, p.num_pid_m, p.num_pid_n, p.group_m, p.xcd_remap, pid,
+                 pid_m, pid_n);
+    pp_tile<AKM, BKM>(p, pid_m * 256, pid_n * 256, S);
+    __syncthreads();   // every wave is done with the stages before the next tile's prologue
+  }
+}
+
+// Split K (see gemm_dma_splitk) on the ping-pong tile.
+template <bool AKM, bool BKM>
+__global__ void __launch_bounds__(512) gemm_pp_splitk(Args p) {
+  GK_DECLARE_STAGES(4, 32768)
+  const int z = blockIdx.x / p.num_programs;
+  const int h = blockIdx.x - z * p.num_programs;
+  int pid, pid_m, pid_n;
+  program_tile(h, p.num_programs, p.num_pid_m, p.num_pid_n, p.group_m, p.xcd_remap, pid, pid_m,
+               pid_n);
+  const int np_all = p.K / 32 + (p.K % 32 ? 1 : 0);
+  const int p1 = np_all - (p.splits - 1 - z) * p.panels_per_split;
+  const int p0 = z == 0 ? 0 : p1 - p.panels_per_split;
+  pp_tile<AKM, BKM, true>(p, pid_m * 256, pid_n * 256, S, p0, p1,
+                          p.W + (int64_t)z * p.M * p.ldw);
 }
 
 // C[i][j] = fp16(W[0][i][j] + W[1][i][j] + ... + W[splits-1][i][j]): the slices added in

@@ -100,7 +100,9 @@ enum {
     GEMM_F16F32_TILE_32x64x128 = 13,     /* 2 wavefronts (1 x 2), 4 stages, read 3 ahead */
     GEMM_F16F32_TILE_64x64x128 = 14,     /* 3 stages, read 3 ahead */
     GEMM_F16F32_TILE_32x32x128 = 15,     /* 1 wavefront, 4 stages, read 3 ahead */
-    GEMM_F16F32_TILE_64x32x128 = 16      /* 2 wavefronts (2 x 1), 4 stages, read 3 ahead */
+    GEMM_F16F32_TILE_64x32x128 = 16,     /* 2 wavefronts (2 x 1), 4 stages, read 3 ahead */
+    GEMM_F16F32_TILE_256x256x32_PP = 17  /* 8 wavefronts (2 x 4), 16x16x32 MFMAs, ping-pong:
+                                            the two waves of a SIMD take turns multiplying */
 };
 
 /* opts.split_k: the library chooses the number of k slices (see gemm_f16f32_opts). */

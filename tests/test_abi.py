@@ -331,18 +331,18 @@ def test_persistent_plans():
         g.ERR_OPTS
 
 
-def test_misaligned_rows_take_the_eight_wavefront_tile():
+def test_misaligned_rows_take_the_ping_pong_tile():
     """Where the table picks the 4-wavefront 256 x 256 tile for aligned rows, misaligned rows
-    (odd leading dimension or a 2-byte aligned start) get the 8-wavefront one."""
+    (odd leading dimension or a 2-byte aligned start) get the 8-wavefront ping-pong one."""
     M = N = K = 4096
     p = plan(M, N, K)
     if p["tile"] != g.TILE_256x256x64:
         pytest.skip("the table does not pick the 4-wavefront 256 x 256 tile here")
-    assert plan(M, N, K, lda=K + 1)["tile"] == g.TILE_256x256x64_W8
-    assert plan(M, N, K, ldb=N + 1)["tile"] == g.TILE_256x256x64_W8
-    assert plan(M, N, K, a=PA + 2)["tile"] == g.TILE_256x256x64_W8
+    assert plan(M, N, K, lda=K + 1)["tile"] == g.TILE_256x256x32_PP
+    assert plan(M, N, K, ldb=N + 1)["tile"] == g.TILE_256x256x32_PP
+    assert plan(M, N, K, a=PA + 2)["tile"] == g.TILE_256x256x32_PP
     assert plan(M, N, K, lda=K + 8)["tile"] == g.TILE_256x256x64
-    assert plan(4095, 4097, 4093)["tile"] == g.TILE_256x256x64_W8
+    assert plan(4095, 4097, 4093)["tile"] == g.TILE_256x256x32_PP
 
 
 def test_struct_layouts_match_the_header(tmp_path):
