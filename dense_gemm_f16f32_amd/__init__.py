@@ -62,7 +62,8 @@ class PlanInfo(ctypes.Structure):
                                               "xcd_remap", "num_pid_m", "num_pid_n",
                                               "num_programs", "launches", "main_m", "main_n",
                                               "a_kmajor", "b_kmajor", "swapped", "threads",
-                                              "persistent", "grid", "splits", "split_depth")
+                                              "persistent", "grid", "splits", "split_depth",
+                                              "strip_n")
                ] + [("workspace_bytes", ctypes.c_int64)]
 
     def as_dict(self) -> dict:

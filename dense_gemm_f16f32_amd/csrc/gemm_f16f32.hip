@@ -228,6 +228,7 @@ int plan_launch(const Problem& pr, int64_t M, int64_t N, const TileDesc* t, int 
   r->swapped = pr.swapped;
   r->splits = 1;
   r->split_depth = 0;
+  r->strip_n = 0;
   r->workspace_bytes = 0;
   return GEMM_F16F32_OK;
 }
@@ -320,12 +321,22 @@ int plan_parts(const Problem& pr, const gemm_f16f32_opts* opts, int64_t ws_bytes
   int64_t Mm = M, Nm = N;
   const bool split =
       !split_k && (o.split_edges == 1 || (o.split_edges == 0 && o.tile == 0));
+  int64_t strip_n = 0;
   if (split && !emptyC) {
     const int64_t rm = M % t->bm, rn = N % t->bn;
     const int64_t full_m = M / t->bm, full_n = N / t->bn;
     if (full_m * full_n >= 128) {
       if (rn > 0 && 4 * rn <= t->bn) Nm = N - rn;
       if (rm > 0 && 4 * rm <= t->bm) Mm = M - rm;
+    }
+    // A right strip of at most 16 columns, with no bottom strip, is computed inside the
+    // ping-pong tile's own launch when each tile row has at least 16 workgroups (one 16-row
+    // block of the strip each); it costs one MFMA per panel in one wave, so it is taken at
+    // any size.
+    if (t->read_ahead == 0 && o.force_generic != 1 && o.persistent != 1 && rn > 0 &&
+        rn <= 16 && full_n >= 16 && Mm == M) {
+      Nm = N - rn;
+      strip_n = rn;
     }
   }
   // A tile chosen here (not forced by the caller) that cannot address the operands with
@@ -345,6 +356,10 @@ int plan_parts(const Problem& pr, const gemm_f16f32_opts* opts, int64_t ws_bytes
   if (split_k) {
     *nparts = 1;
     return plan_split(pr, L, &parts[0].r);
+  }
+  if (strip_n > 0 && pp->r.tile == t->id) {
+    pp->r.strip_n = (int32_t)strip_n;
+    Nm = N;   // no separate launch for it
   }
   ++pp;
   const int64_t strips[3][4] = {{0, Nm, Mm, N - Nm}, {Mm, 0, M - Mm, Nm}, {Mm, Nm, M - Mm, N - Nm}};
@@ -375,8 +390,10 @@ hipError_t launch_layout(const gemm_f16f32_plan_info& r, const gk::Args& a, bool
         hipLaunchKernelGGL((gk::gemm_pp_splitk<AKM, BKM>), grid, block, 0, stream, a);
       else if (r.persistent)
         hipLaunchKernelGGL((gk::gemm_pp_persistent<AKM, BKM>), grid, block, 0, stream, a);
+      else if (a.strip_n > 0)
+        hipLaunchKernelGGL((gk::gemm_pp<AKM, BKM, true>), grid, block, 0, stream, a);
       else
-        hipLaunchKernelGGL((gk::gemm_pp<AKM, BKM>), grid, block, 0, stream, a);
+        hipLaunchKernelGGL((gk::gemm_pp<AKM, BKM, false>), grid, block, 0, stream, a);
       return hipGetLastError();
     }
   } else if (r.splits > 1) {
@@ -438,6 +455,7 @@ int launch_part(const Problem& pr, const Part& pt, float* ws, hipStream_t s) {
   a.ldw = cdiv(pt.N, 4) * 4;
   a.splits = r.splits;
   a.panels_per_split = r.splits > 1 ? r.split_depth / r.bk : 0;
+  a.strip_n = r.strip_n;
   const bool odd = (((uintptr_t)a.A | (uintptr_t)a.B) & 3) != 0 || ((pr.lda | pr.ldb) & 1) != 0;
   hipError_t e = hipSuccess;
   switch (r.tile) {

@@ -64,6 +64,9 @@ struct Args {
   float* W;
   int64_t ldw;
   int32_t splits, panels_per_split;
+  // Ping-pong tile only (gemm_pp with a strip): the strip_n (1..16) columns of C right of the
+  // N launched ones, computed by the launch's own workgroups (see pp_tile).
+  int32_t strip_n;
 };
 
 // ---------------------------------------------------------------------------------------
@@ -955,10 +958,33 @@ struct PPTile {   // one wave's block, in the terms store_tile uses
   using Acc = float4v;
 };
 
-template <bool AKM, bool BKM, bool SPLIT = false>
+// The strip.  When the last tile column would hold only a few (1..16) columns, the planner
+// launches the grid over the columns left of them, and the workgroups of each tile row compute
+// those columns too: 16 rows each, the workgroup in tile column c taking the rows
+// 16c .. 16c+15 of its tile row (so the 16 workgroups of a tile row cover its 256 rows).  The
+// rows' A operands are already in the registers of one wave (wave c / 8, the one holding rows
+// 128 (c/8) .. +127), which issues one more MFMA per panel: that A block times a 32-deep
+// B block whose column j is the strip's column j (and whose columns past the strip only feed
+// results that are never stored).  That B block is staged per panel by the same wave in 1 KiB
+// beside the stage, by one more DMA load.  The sum of a strip element is the same sequence
+// of 32-deep MFMA steps as in any tile, so the strip's bits are those of a separate launch.
+template <bool BKM>
+struct StripB {
+  // Load slot of lane l in the 1 KiB staging area: x-major B -> k row l/2, 8 columns at
+  // 8 (l%2); k-major B -> strip column l/4, 8 k values at 8 (l%4).
+  __device__ static int64_t elem(int lane, int64_t x0, int64_t k0, int64_t ld) {
+    return BKM ? (x0 + (lane >> 2)) * ld + k0 + 8 * (lane & 3)
+               : (k0 + (lane >> 1)) * ld + x0 + 8 * (lane & 1);
+  }
+  // LDS byte offset, inside the area, of element (strip column j, panel k value kk).
+  __device__ static int at(int j, int kk) { return BKM ? j * 64 + kk * 2 : kk * 32 + j * 2; }
+};
+
+template <bool AKM, bool BKM, bool SPLIT = false, bool STRIP = false>
 __device__ __forceinline__ void pp_tile(const Args& p, int m0, int n0,
                                         char GK_LDS* const (&S)[kMaxStages], int p0 = 0,
                                         int p1 = 0, float* ws = nullptr) {
+  static_assert(!(SPLIT && STRIP), "no strip with split K");
   using T = PPTile;
   using OA = Opnd<256, 32, AKM, 2, 8, 16>;   // operand reads: 2 waves along M
   using OB = Opnd<256, 32, BKM, 4, 8, 16>;   // operand reads: 4 waves along N
@@ -992,10 +1018,30 @@ __device__ __forceinline__ void pp_tile(const Args& p, int m0, int n0,
   uint16_t last_a = 0, last_b = 0;
   const int patch_a = last_element_slot<OA>(m0, p.M, p.K, p.A, extA, tid, last_a);
   const int patch_b = last_element_slot<OB>(n0, p.N, p.K, p.B, extB, tid, last_b);
+  // The strip (see StripB): this tile column's 16-row block sb, if any, is computed by wave
+  // sb / 8.  Its last element (the matrix's last) is rewritten like the operands' (see
+  // last_element_slot) by the lane whose load slot holds it.
+  constexpr int STRIP_AT = A_BYTES + OB::BYTES;   // staging area inside a stage
+  const int sb = n0 / 256;
+  const bool strip_wave = STRIP && sb < 16 && w == (sb >> 3);
+  const int strip_tm = sb & 7;
+  const int64_t sx0 = p.N;                        // first strip column
+  const int64_t extBs = STRIP ? extent<BKM>(p.N + p.strip_n, p.K, p.ldb) : 0;
+  int patch_s = -1;
+  uint16_t last_s = 0;
+  if (strip_wave && p.K > 0) {
+    const int j = p.strip_n - 1, kk = (p.K - 1 - kofs) % BK;
+    const int q = BKM ? 4 * j + (kk >> 3) : 2 * kk + (j >> 3);
+    if (q == lane) {
+      patch_s = StripB<BKM>::at(j, kk);
+      last_s = __builtin_amdgcn_raw_buffer_load_b16(make_rsrc(p.B + extBs - 1, 2), 0u, 0, 0);
+    }
+  }
   auto patch = [&](char GK_LDS* base) __attribute__((always_inline)) {
     if (!has_last) return;
     if (patch_a >= 0) *(uint16_t GK_LDS*)(base + patch_a) = last_a;
     if (patch_b >= 0) *(uint16_t GK_LDS*)(base + A_BYTES + patch_b) = last_b;
+    if (STRIP && patch_s >= 0) *(uint16_t GK_LDS*)(base + STRIP_AT + patch_s) = last_s;
   };
   // This wave's share of full panel u (k0 >= 0); panels past the end load zeros.
   auto issue = [&](int u, char GK_LDS* base) __attribute__((always_inline)) {
@@ -1012,6 +1058,45 @@ __device__ __forceinline__ void pp_tile(const Args& p, int m0, int n0,
     head_store<OB>(vb, base + A_BYTES, w, lane);
   };
 
+  auto issue_strip = [&](int u, char GK_LDS* base) __attribute__((always_inline)) {
+    const bool live = u < np;
+    const int64_t k0 = (int64_t)kofs + (int64_t)u * BK;
+    const int64_t e0 = BKM ? sx0 * p.ldb + k0 : k0 * p.ldb + sx0;
+    const __amdgpu_buffer_rsrc_t r =
+        make_rsrc(p.B + (live ? e0 : 0), live ? 2 * (extBs - e0) : 0);
+    const int64_t off = StripB<BKM>::elem(lane, sx0, k0, p.ldb) - e0;
+    buffer_load_lds16(r, (void GK_LDS*)(base + STRIP_AT), 2u * (uint32_t)off);
+  };
+  // head panel of the strip (k0 = kofs < 0): through registers, k < 0 read as zero
+  auto head_strip = [&](char GK_LDS* base) __attribute__((always_inline)) {
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(p.B, 2 * extBs);
+    uint16_t h[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int64_t k = BKM ? (int64_t)kofs + 8 * (lane & 3) + e : (int64_t)kofs + (lane >> 1);
+      const int64_t x = BKM ? sx0 + (lane >> 2) : sx0 + 8 * (lane & 1) + e;
+      h[e] = k >= 0 ? __builtin_amdgcn_raw_buffer_load_b16(
+                          r, (uint32_t)(2 * elem_off<BKM>(x, k, p.ldb)), 0, 0)
+                    : (uint16_t)0;
+    }
+    u32x4 v;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) v[d] = (uint32_t)h[2 * d] | ((uint32_t)h[2 * d + 1] << 16);
+    *(u32x4 GK_LDS*)(base + STRIP_AT + lane * 16) = v;
+  };
+  half8 rs;   // the strip's B operand of the current panel
+  auto fetch_strip = [&](const char GK_LDS* st) __attribute__((always_inline)) {
+    if constexpr (BKM) {
+      rs = *(const half8 GK_LDS*)(st + STRIP_AT + StripB<BKM>::at(lane & 15, 8 * (lane >> 4)));
+    } else {
+      const int g = lane >> 4, i = lane & 15;
+      const char GK_LDS* q = st + STRIP_AT + StripB<BKM>::at((i & 3) * 4, g * 8 + (i >> 2));
+      short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((short4v GK_LDS*)q);
+      short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((short4v GK_LDS*)(q + 4 * 32));
+      rs = __builtin_bit_cast(half8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+  };
+
   int oa[OA::NOFF], ob[OB::NOFF];
   operand_offsets<OA>(oa, wm, lane, 0);
   operand_offsets<OB>(ob, wn, lane, A_BYTES);
@@ -1023,15 +1108,33 @@ __device__ __forceinline__ void pp_tile(const Args& p, int m0, int n0,
     for (int tn = 0; tn < TN; ++tn) rb[tn] = read_operand<OB>(st, ob, tn, 0);
   };
 
+  // Waits until this wave's share of the panel before the last two it issued has landed
+  // (the strip's wave has one load more per panel).
+  auto wait_panel = [&]() __attribute__((always_inline)) {
+    if (STRIP && strip_wave)
+      wait_vmcnt<2 * (NL + 1)>();
+    else
+      wait_vmcnt<2 * NL>();
+  };
+
   // Prologue: panels 0, 1 and 2 (the head through registers), then panel 0 has landed.
   if (np > 0) {
     if (rk)
       head(S[0]);
     else
       issue(0, S[0]);
-    issue(1, S[1]);
-    issue(2, S[2]);
-    wait_vmcnt<2 * NL>();
+    if (STRIP && strip_wave) {
+      if (rk)
+        head_strip(S[0]);
+      else
+        issue_strip(0, S[0]);
+    }
+#pragma unroll
+    for (int u = 1; u < 3; ++u) {
+      issue(u, S[u]);
+      if (STRIP && strip_wave) issue_strip(u, S[u]);
+    }
+    wait_panel();
     if (np == 1) patch(S[0]);
   }
 
@@ -1040,24 +1143,36 @@ __device__ __forceinline__ void pp_tile(const Args& p, int m0, int n0,
   for (int tm = 0; tm < TM; ++tm)
 #pragma unroll
     for (int tn = 0; tn < TN; ++tn) acc[tm][tn] = typename T::Acc{};
-  mfma16_pin_zero<T>(acc);
+  typename T::Acc acc_s = typename T::Acc{};   // the strip block (strip wave only)
 
+  // The MFMAs go through the builtin here, so that the compiler sees them: this kernel's
+  // register allocation moves accumulators between register files around them, and the
+  // compiler then keeps the wait states such moves need.
+  // The builtins touch no memory, so scheduling barriers keep them inside their phase.
   auto multiply = [&]() __attribute__((always_inline)) {
-    // the operand registers were written by LDS reads before the phase's barrier; a few
-    // wait states more cover any register copy the compiler placed after them.  While it
-    // multiplies, the wave has the higher issue priority on its SIMD.
-    asm volatile("s_setprio 1\n\ts_nop 4" ::: "memory");
+    // While it multiplies, the wave has the higher issue priority on its SIMD.
+    asm volatile("s_setprio 1" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int tm = 0; tm < TM; ++tm)
 #pragma unroll
-      for (int tn = 0; tn < TN; ++tn) mfma16(acc[tm][tn], ra[tm], rb[tn]);
+      for (int tn = 0; tn < TN; ++tn)
+        acc[tm][tn] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ra[tm], rb[tn], acc[tm][tn], 0, 0, 0);
+    if (STRIP && strip_wave) {
+#pragma unroll
+      for (int tm = 0; tm < TM; ++tm)
+        if (tm == strip_tm) acc_s = __builtin_amdgcn_mfma_f32_16x16x32_f16(ra[tm], rs, acc_s, 0, 0, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
     asm volatile("s_setprio 0" ::: "memory");
   };
   // Panel u from stage j = u mod 4.
   auto panel = [&](int u, int j) __attribute__((always_inline)) {
     fetch(S[j]);
+    if (STRIP && strip_wave) fetch_strip(S[j]);
     issue(u + 3, S[(j + 3) % NS]);     // panel u-1's stage, read by every wave by now
-    wait_vmcnt<2 * NL>();              // this wave's share of panel u+1 has landed
+    if (STRIP && strip_wave) issue_strip(u + 3, S[(j + 3) % NS]);
+    wait_panel();                      // this wave's share of panel u+1 has landed
     if (u + 2 == np) patch(S[(j + 1) % NS]);   // panel u+1 is the last one
     lds_barrier();
     multiply();
@@ -1074,20 +1189,38 @@ __device__ __forceinline__ void pp_tile(const Args& p, int m0, int n0,
     if (w < 4) lds_barrier();          // the same number of barriers in every wave
   }
   wait_vmcnt<0>();                     // the empty loads past the end, before LDS is freed
-  mfma16_drain<T>(acc);
-  if constexpr (SPLIT)
+  if constexpr (SPLIT) {
     store_partial<T>(p, ws, acc, m0, n0, wm, wn, lane);
-  else
+  } else {
     store_tile<T>(p, acc, m0, n0, wm, wn, lane);
+    if constexpr (STRIP) {
+      if (strip_wave) {
+        // lane l holds rows 4 (l/16) + v, v = 0..3, of the block, strip column l % 16
+        const int j = lane & 15, r0 = m0 + 16 * sb + 4 * (lane >> 4);
+        const int64_t extC = (int64_t)(p.M - 1) * p.ldc + p.N + p.strip_n;
+        const __amdgpu_buffer_rsrc_t rc = make_rsrc(p.C, 2 * extC);
+        if (j < p.strip_n) {
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            if (r0 + v < p.M) {
+              const _Float16 h = (_Float16)acc_s[v];
+              __builtin_amdgcn_raw_buffer_store_b16(
+                  __builtin_bit_cast(uint16_t, h), rc,
+                  (uint32_t)(2 * ((int64_t)(r0 + v) * p.ldc + p.N + j)), 0, 0);
+            }
+        }
+      }
+    }
+  }
 }
 
-template <bool AKM, bool BKM>
+template <bool AKM, bool BKM, bool STRIP>
 __global__ void __launch_bounds__(512) gemm_pp(Args p) {
-  GK_DECLARE_STAGES(4, 32768)
+  GK_DECLARE_STAGES(4, 32768 + (STRIP ? 1024 : 0))
   int pid, pid_m, pid_n;
   program_tile(blockIdx.x, p.num_programs, p.num_pid_m, p.num_pid_n, p.group_m, p.xcd_remap,
                pid, pid_m, pid_n);
-  pp_tile<AKM, BKM>(p, pid_m * 256, pid_n * 256, S);
+  pp_tile<AKM, BKM, false, STRIP>(p, pid_m * 256, pid_n * 256, S);
 }
 
 // The persistent grouped schedule (see gemm_dma_persistent) on the ping-pong tile.

@@ -175,6 +175,10 @@ typedef struct gemm_f16f32_plan_info {
                               splits * num_programs when split) */
     int32_t splits;        /* k slices (1 = no split K) */
     int32_t split_depth;   /* k values per slice L (0 = no split K) */
+    int32_t strip_n;       /* columns of C right of main_n (rows, when swapped, below it)
+                              that the main launch computes itself: the ping-pong tile takes a
+                              last tile column of 1-16 columns into the tile rows' workgroups
+                              (0 = none; otherwise such a sliver is a launch of its own) */
     int64_t workspace_bytes; /* workspace the call needs, splits * M' * roundup(N', 4) * 4 bytes
                               where M' x N' is the launch's C (M x N, or N x M when swapped):
                               slice z's fp32 sums at workspace + 4 (z M' + i) roundup(N', 4) + 4 j;

@@ -164,8 +164,15 @@ def test_plans_for_the_five_workloads():
     assert (p["launches"], p["main_m"], p["main_n"]) == (2, 4095, 4096)
     p = plan(4095, 4097, 4093, tile=g.TILE_256x256x64, group_m=6)
     assert (p["num_pid_m"], p["num_pid_n"], p["num_programs"], p["launches"]) == (16, 17, 272, 1)
+    # the library's own plan: the ping-pong tile (odd leading dimensions) computes the
+    # 1-column sliver inside its own launch
     p = plan(4095, 4097, 4093)
-    assert p["launches"] == 2 and p["main_n"] == 4096
+    assert p["tile"] == g.TILE_256x256x32_PP
+    assert (p["launches"], p["main_n"], p["strip_n"], p["num_pid_n"]) == (1, 4096, 1, 16)
+    # the same shape with aligned rows keeps the 256 x 256 x 64 tile and a second launch
+    p = plan(4095, 4097, 4093, lda=4096, ldb=4104, ldc=4104)
+    if p["tile"] == g.TILE_256x256x64:
+        assert (p["launches"], p["main_n"], p["strip_n"]) == (2, 4096, 0)
 
 
 def test_path_selection():
