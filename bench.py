@@ -25,7 +25,6 @@ the same launches run for 3 s while the XCD clocks and the socket power are samp
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -37,32 +36,10 @@ if ROOT not in sys.path:
 
 METRIC = "fp16-in/fp32-acc GEMM TFLOP/s at 8192³ on 1 MI355X; % of fp16 MFMA peak"
 PEAK_TFLOPS = 2500.0          # MI355X published dense fp16 matrix peak
-CSRC = os.path.join(ROOT, "dense_gemm_f16f32_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
-KERNEL_SOURCES = ("gemm_kernels.hpp", "gemm_tiles.hpp")
-
-
-def strip_comments(text: str) -> str:
-    """C++ source without comments and with runs of white space collapsed (the sources have
-    no string literals that contain comment markers)."""
-    import re
-    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
-    text = re.sub(r"//[^\n]*", " ", text)
-    return " ".join(text.split())
-
-
-def kernel_source_hash() -> str:
-    """sha256 (first 16 hex digits) of the files that fix the kernels' code -- the device code
-    and the tile configurations -- with comments and white space removed, so that only a code
-    change voids the traffic record.  The planner and its dispatch table are left out: they
-    choose the launch configuration, which the record's key already names."""
-    h = hashlib.sha256()
-    for name in KERNEL_SOURCES:
-        with open(os.path.join(CSRC, name)) as f:
-            h.update(name.encode() + b"\0" + strip_comments(f.read()).encode())
-    return h.hexdigest()[:16]
+from dense_gemm_f16f32_amd.build import kernel_source_hash, strip_comments  # noqa: E402,F401
 
 
 def measured_traffic(workload: str, tile: int, group_m: int, remap: int):

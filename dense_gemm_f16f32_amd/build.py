@@ -22,6 +22,31 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
 
 LLVM = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "llvm", "bin")
 
+KERNEL_SOURCES = ("gemm_kernels.hpp", "gemm_tiles.hpp")
+
+
+def strip_comments(text: str) -> str:
+    """C++ source without comments and with runs of white space collapsed (the sources have
+    no string literals that contain comment markers)."""
+    import re
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
+def kernel_source_hash() -> str:
+    """sha256 (first 16 hex digits) of the files that fix the kernels' code -- the device code
+    and the tile configurations -- with comments and white space removed, so that only a code
+    change counts.  The planner and its dispatch table are left out: they choose the launch
+    configuration.  The dispatch table and the HBM-traffic record carry the hash they were
+    measured at."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(PKG, "csrc", name)) as f:
+            h.update(name.encode() + b"\0" + strip_comments(f.read()).encode())
+    return h.hexdigest()[:16]
+
 # Kernels whose 16x16x32 MFMAs are inline asm (the 256 x 256 x 64 tile on 2 x 2 wavefronts:
 # its DMA, persistent, split-K and generic forms).  The compiler's hazard checks do not see
 # those MFMAs, so the code provides the wait states itself (gemm_kernels.hpp, mfma16).

@@ -17,7 +17,8 @@ tiles within 5 % of the fastest are timed again in six interleaved rounds and co
 median.  Every forced configuration must also reproduce the first
 configuration's bits (all tiles add the same MFMA k steps per element).
 
-    python -m dense_gemm_f16f32_amd.tune [--out PATH] [--quick]
+    python -m dense_gemm_f16f32_amd.tune [--out PATH] [--quick] [--k K,...] [--json PATH]
+    python -m dense_gemm_f16f32_amd.tune --from-json a.json,b.json,...   (merge partial sweeps)
 
 `--split-sweep` instead times split K (gemm_f16f32_strided_ws with split_k = S, the tile
 chosen by the planner for each slice shape) for S in 1, 2, 4, ..., 32 and the automatic
@@ -193,10 +194,11 @@ def split_sweep(torch, shapes=None, splits=None):
         print(json.dumps(row), flush=True)
 
 
-def write_table(path, results, device):
+def write_table(path, results, device, source_hash):
     lines = [
         "// Tile configuration and GROUP_SIZE_M per shape class, written by",
-        "// dense_gemm_f16f32_amd/tune.py from device-time sweeps on " + device + ".",
+        "// dense_gemm_f16f32_amd/tune.py from device-time sweeps on " + device + ",",
+        f"// kernel source hash {source_hash} (build.kernel_source_hash at the time of the sweep).",
         "// Key: rounded log2 of M, N (32 .. 8192) and K (64 .. 8192); group 0 = the tile's",
         "// default.  Columns: log2 M, log2 N, log2 K, tile, group; the comment gives the",
         "// chosen configuration's time and the time of the choice it replaced (same sweep), us.",
@@ -222,7 +224,11 @@ def main():
     ap.add_argument("--json", default=None, help="also write every timing as JSON here")
     ap.add_argument("--quick", action="store_true", help="skip grids above 4096 workgroups")
     ap.add_argument("--from-json", default=None,
-                    help="only rewrite the table from a JSON file of an earlier sweep")
+                    help="only rewrite the table from JSON files of earlier sweeps (comma-"
+                         "separated; their shape classes are merged)")
+    ap.add_argument("--k", default=None,
+                    help="sweep only these K values of the grid (comma-separated); with "
+                         "--json, the partial results can be merged with --from-json")
     ap.add_argument("--split-sweep", action="store_true",
                     help="time split K per split count instead (no table is written)")
     ap.add_argument("--shapes", default=None,
@@ -243,10 +249,18 @@ def main():
         split_sweep(torch, shapes, splits)
         return
     if args.from_json:
-        with open(args.from_json) as f:
-            rec = json.load(f)
-        write_table(args.out, rec["results"], rec["device"])
-        print(f"wrote {args.out} ({len(rec['results'])} shape classes)")
+        results, devices, hashes = [], set(), set()
+        for path in args.from_json.split(","):
+            with open(path) as f:
+                rec = json.load(f)
+            results += rec["results"]
+            devices.add(rec["device"])
+            hashes.add(rec.get("source_hash", "unknown"))
+        if len(hashes) != 1:
+            raise SystemExit(f"sweeps of different kernel sources: {sorted(hashes)}")
+        results.sort(key=lambda r: (r["K"], r["M"], r["N"]))
+        write_table(args.out, results, " / ".join(sorted(devices)), hashes.pop())
+        print(f"wrote {args.out} ({len(results)} shape classes)")
         return
     import torch
 
@@ -254,9 +268,12 @@ def main():
     props = torch.cuda.get_device_properties(0)
     device = f"{props.name} ({getattr(props, 'gcnArchName', 'gfx950').split(':')[0]}, " \
              f"{props.multi_processor_count} CUs)"
+    from dense_gemm_f16f32_amd.build import kernel_source_hash
+    source_hash = kernel_source_hash()
     results = []
     t0 = time.time()
-    for K in K_GRID:
+    k_grid = [int(k) for k in args.k.split(",")] if args.k else K_GRID
+    for K in k_grid:
         for M in MN_GRID:
             for N in MN_GRID:
                 r = tune_shape(torch, M, N, K, args.quick)
@@ -265,10 +282,11 @@ def main():
                                                     "auto_us")}
                                  | {"best_us": r["us"][str(r["best_tile"])],
                                     "elapsed_s": round(time.time() - t0, 1)}), flush=True)
-    write_table(args.out, results, device)
+    if not args.k:
+        write_table(args.out, results, device, source_hash)
     if args.json:
         with open(args.json, "w") as f:
-            json.dump({"device": device, "results": results}, f)
+            json.dump({"device": device, "source_hash": source_hash, "results": results}, f)
     print(f"wrote {args.out} ({len(results)} shape classes)", flush=True)
 
 

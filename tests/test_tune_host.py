@@ -25,7 +25,7 @@ def fake_results():
 def test_written_rows_parse_back(tmp_path, monkeypatch):
     out = tmp_path / "table.inc"
     rows = fake_results()
-    tune.write_table(str(out), rows, "test device")
+    tune.write_table(str(out), rows, "test device", "0123456789abcdef")
     import test_abi
     monkeypatch.setattr(test_abi, "TUNE_TABLE", str(out))
     parsed = tune_entries()
@@ -56,3 +56,30 @@ def test_rewrite_from_json(tmp_path):
     finally:
         sys.argv = argv
     assert out.read_text().count("\n{") == len(rec["results"])
+
+
+def test_merge_partial_sweeps_with_the_source_hash(tmp_path):
+    rows = fake_results()
+    a, b = tmp_path / "a.json", tmp_path / "b.json"
+    a.write_text(json.dumps({"device": "d", "source_hash": "00ff00ff00ff00ff",
+                             "results": [r for r in rows if r["K"] == 64]}))
+    b.write_text(json.dumps({"device": "d", "source_hash": "00ff00ff00ff00ff",
+                             "results": [r for r in rows if r["K"] != 64]}))
+    out = tmp_path / "t.inc"
+    import sys
+    argv = sys.argv
+    try:
+        sys.argv = ["tune", "--from-json", f"{a},{b}", "--out", str(out)]
+        tune.main()
+        text = out.read_text()
+        assert text.count("\n{") == len(rows) and "kernel source hash 00ff00ff00ff00ff" in text
+        b.write_text(json.dumps({"device": "d", "source_hash": "1111111111111111",
+                                 "results": [r for r in rows if r["K"] != 64]}))
+        sys.argv = ["tune", "--from-json", f"{a},{b}", "--out", str(out)]
+        try:
+            tune.main()
+            raise AssertionError("sweeps of different kernel sources were merged")
+        except SystemExit:
+            pass
+    finally:
+        sys.argv = argv
