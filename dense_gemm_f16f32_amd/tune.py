@@ -287,7 +287,8 @@ def main():
     if args.json:
         with open(args.json, "w") as f:
             json.dump({"device": device, "source_hash": source_hash, "results": results}, f)
-    print(f"wrote {args.out} ({len(results)} shape classes)", flush=True)
+    print(f"{'wrote ' + args.out if not args.k else 'swept'} ({len(results)} shape classes)",
+          flush=True)
 
 
 if __name__ == "__main__":

@@ -83,3 +83,14 @@ def test_merge_partial_sweeps_with_the_source_hash(tmp_path):
             pass
     finally:
         sys.argv = argv
+
+
+def test_shipped_table_was_measured_on_the_shipped_kernels():
+    """The dispatch table's header names the kernel source hash it was swept at; it must be
+    the hash of the kernels that ship (re-run the sweep after changing them)."""
+    import re
+    from dense_gemm_f16f32_amd.build import kernel_source_hash
+    text = open(tune.TABLE).read()
+    m = re.search(r"kernel source hash ([0-9a-f]{16})", text)
+    assert m, "the table names no kernel source hash"
+    assert m.group(1) == kernel_source_hash()
