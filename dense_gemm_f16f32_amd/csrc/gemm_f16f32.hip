@@ -51,13 +51,14 @@ int heuristic_tile(int64_t M, int64_t N) {
 }
 
 // The dispatch table measured offline by tune.py: for each shape class (rounded log2 of M,
-// N and K) the fastest tile and, where it mattered, GROUP_SIZE_M (0 = the tile's default).
+// N and K) the fastest tile and, where it mattered, GROUP_SIZE_M (0 = the tile's default) and
+// the XCD permutation (0 = on, the default; 2 = off).
 struct TuneEntry {
-  int8_t lm, ln, lk, tile, group;
+  int8_t lm, ln, lk, tile, group, remap;
 };
 constexpr TuneEntry kTune[] = {
 #include "tune_table.inc"
-    {-1, -1, -1, 0, 0}};  // end marker
+    {-1, -1, -1, 0, 0, 0}};  // end marker
 
 int log2_class(int64_t x, int lo, int hi) {
   const int l = x < 1 ? lo : (int)std::lround(std::log2((double)x));
@@ -65,7 +66,7 @@ int log2_class(int64_t x, int lo, int hi) {
 }
 
 struct Choice {
-  int tile, group;
+  int tile, group, remap;   // remap as in gemm_f16f32_opts: 0 default (on), 1 on, 2 off
 };
 
 // Tile and group size for an M x N x K launch: the table's entry for its shape class, else
@@ -77,10 +78,10 @@ struct Choice {
 // 9 % on 4096^3 with odd leading dimensions, level at 8192^3).
 Choice choose_tile(int64_t M, int64_t N, int64_t K, bool aligned) {
   const int lm = log2_class(M, 5, 13), ln = log2_class(N, 5, 13), lk = log2_class(K, 6, 13);
-  Choice c = {heuristic_tile(M, N), 0};
+  Choice c = {heuristic_tile(M, N), 0, 0};
   for (const TuneEntry& e : kTune)
     if (e.lm == lm && e.ln == ln && e.lk == lk && find_tile(e.tile) != nullptr) {
-      c = {e.tile, e.group};
+      c = {e.tile, e.group, e.remap};
       break;
     }
   if (!aligned && c.tile == GEMM_F16F32_TILE_256x256x64) c.tile = GEMM_F16F32_TILE_256x256x32_PP;
@@ -184,7 +185,7 @@ struct Part {
 
 // Fills r for one launch of tile `tile` over M x N (no argument checks here).
 int plan_launch(const Problem& pr, int64_t M, int64_t N, const TileDesc* t, int group,
-                const gemm_f16f32_opts& o, gemm_f16f32_plan_info* r) {
+                int remap, const gemm_f16f32_opts& o, gemm_f16f32_plan_info* r) {
   const int64_t kMax = (int64_t)1 << 31;
   const bool dma = !o.force_generic;
   // 32-bit in-kernel offsets: one panel's stored rows of A (bm rows if k-major, else one k row
@@ -202,7 +203,7 @@ int plan_launch(const Problem& pr, int64_t M, int64_t N, const TileDesc* t, int 
   r->bk = dma ? t->bk : gk::kBK;
   r->threads = 64 * t->wm * t->wn;
   r->group_m = o.group_m ? o.group_m : (group ? group : t->default_group);
-  r->xcd_remap = (o.xcd_remap == 2) ? 0 : 1;
+  r->xcd_remap = ((o.xcd_remap ? o.xcd_remap : remap) == 2) ? 0 : 1;
   const bool empty = (M == 0 || N == 0);
   r->num_pid_m = empty ? 0 : (int32_t)cdiv(M, t->bm);
   r->num_pid_n = empty ? 0 : (int32_t)cdiv(N, t->bn);
@@ -316,7 +317,7 @@ int plan_parts(const Problem& pr, const gemm_f16f32_opts* opts, int64_t ws_bytes
 
   const bool aligned = aligned_rows(pr);
   // A split problem is chosen for as the slices' own shape, M x N x L.
-  const Choice ch = o.tile ? Choice{o.tile, 0} : choose_tile(M, N, split_k ? L : K, aligned);
+  const Choice ch = o.tile ? Choice{o.tile, 0, 0} : choose_tile(M, N, split_k ? L : K, aligned);
   const TileDesc* t = find_tile(ch.tile);
   int64_t Mm = M, Nm = N;
   const bool split =
@@ -342,16 +343,17 @@ int plan_parts(const Problem& pr, const gemm_f16f32_opts* opts, int64_t ws_bytes
   // A tile chosen here (not forced by the caller) that cannot address the operands with
   // 32-bit offsets -- a leading dimension of about 2^24 elements or more -- gives way to the
   // 32 x 32 x 64 tile, whose panels store the fewest rows, before the call is refused.
-  auto plan_or_fallback = [&](int64_t m, int64_t n, const TileDesc* tt, int group, bool forced,
-                              const gemm_f16f32_opts& oo, gemm_f16f32_plan_info* r) {
-    int rc = plan_launch(pr, m, n, tt, group, oo, r);
+  auto plan_or_fallback = [&](int64_t m, int64_t n, const TileDesc* tt, int group, int remap,
+                              bool forced, const gemm_f16f32_opts& oo,
+                              gemm_f16f32_plan_info* r) {
+    int rc = plan_launch(pr, m, n, tt, group, remap, oo, r);
     if (rc == GEMM_F16F32_ERR_TOO_LARGE && !forced && tt->id != GEMM_F16F32_TILE_32x32x64)
-      rc = plan_launch(pr, m, n, find_tile(GEMM_F16F32_TILE_32x32x64), 0, oo, r);
+      rc = plan_launch(pr, m, n, find_tile(GEMM_F16F32_TILE_32x32x64), 0, 0, oo, r);
     return rc;
   };
   Part* pp = parts;
   pp->m_off = 0, pp->n_off = 0, pp->M = Mm, pp->N = Nm;
-  int rc = plan_or_fallback(Mm, Nm, t, ch.group, o.tile != 0, o, &pp->r);
+  int rc = plan_or_fallback(Mm, Nm, t, ch.group, ch.remap, o.tile != 0, o, &pp->r);
   if (rc != GEMM_F16F32_OK) return rc;
   if (split_k) {
     *nparts = 1;
@@ -370,7 +372,7 @@ int plan_parts(const Problem& pr, const gemm_f16f32_opts* opts, int64_t ws_bytes
     if (st[2] == 0 || st[3] == 0) continue;
     pp->m_off = st[0], pp->n_off = st[1], pp->M = st[2], pp->N = st[3];
     const Choice cs = choose_tile(st[2], st[3], K, aligned);
-    rc = plan_or_fallback(st[2], st[3], find_tile(cs.tile), cs.group, false, os, &pp->r);
+    rc = plan_or_fallback(st[2], st[3], find_tile(cs.tile), cs.group, cs.remap, false, os, &pp->r);
     if (rc != GEMM_F16F32_OK) return rc;
     ++pp;
   }

@@ -140,19 +140,29 @@ def tune_shape(torch, M, N, K, quick=False):
             best = current
     elif current in times and times[best] > (1.0 - MARGIN) * times[current]:
         best = current
-    group, group_times = 0, {}
+    # GROUP_SIZE_M and the XCD permutation (on: key "G", off: key "Gx"), for grids large
+    # enough for the order to matter; the tile's default (its G, permutation on) stays unless
+    # another order is clearly faster in interleaved rounds
+    group, remap, group_times = 0, 0, {}
     if programs(M, N, best) >= 128:
-        for G in GROUPS:
-            opts = dict(tile=best, group_m=G, **split_off)
-            group_times[G] = graph_time_us(torch, lambda: g.matmul(A, B, C, **opts))
-        gbest = min(group_times, key=group_times.get)
-        # keep the tile's default unless another group size is clearly faster
         rc, info = g.gemm_f16f32_plan(M, N, K, A.data_ptr(), B.data_ptr(), C.data_ptr(), K, N,
                                       N, opts=dict(tile=best))
-        default_g = info["group_m"]
-        if group_times[gbest] < (1.0 - MARGIN) * group_times.get(default_g, times[best]):
-            group = gbest
-    return {"M": M, "N": N, "K": K, "best_tile": best, "group_m": group, "current": current,
+        default_key = str(info["group_m"])
+        keys = [f"{G}{x}" for G in GROUPS for x in ("", "x")]
+        fns = {k: (lambda k=k: g.matmul(A, B, C, tile=best, group_m=int(k.rstrip("x")),
+                                        xcd_remap=g.REMAP_OFF if k.endswith("x") else
+                                        g.REMAP_ON, **split_off)) for k in keys}
+        runs = {k: [] for k in keys}
+        for r in range(2):
+            for k in (keys if r % 2 == 0 else keys[::-1]):
+                runs[k].append(graph_time_us(torch, fns[k], target_us=1500.0))
+        group_times = {k: sum(v) / len(v) for k, v in runs.items()}
+        gbest = min(group_times, key=group_times.get)
+        if gbest != default_key and \
+                group_times[gbest] < (1.0 - MARGIN) * group_times[default_key]:
+            group, remap = int(gbest.rstrip("x")), (2 if gbest.endswith("x") else 0)
+    return {"M": M, "N": N, "K": K, "best_tile": best, "group_m": group, "remap": remap,
+            "current": current,
             "us": {str(k): round(v, 2) for k, v in times.items()},
             "ab_us": {str(k): round(v, 2) for k, v in ab.items()},
             "group_us": {str(k): round(v, 2) for k, v in group_times.items()},
@@ -200,8 +210,9 @@ def write_table(path, results, device, source_hash):
         "// dense_gemm_f16f32_amd/tune.py from device-time sweeps on " + device + ",",
         f"// kernel source hash {source_hash} (build.kernel_source_hash at the time of the sweep).",
         "// Key: rounded log2 of M, N (32 .. 8192) and K (64 .. 8192); group 0 = the tile's",
-        "// default.  Columns: log2 M, log2 N, log2 K, tile, group; the comment gives the",
-        "// chosen configuration's time and the time of the choice it replaced (same sweep), us.",
+        "// default; remap 0 = XCD permutation on (default), 2 = off.  Columns: log2 M, log2 N,",
+        "// log2 K, tile, group, remap; the comment gives the chosen configuration's time and",
+        "// the time of the choice it replaced (same sweep), us.",
     ]
     for r in results:
         lm, ln, lk = (int(round(math.log2(r[x]))) for x in ("M", "N", "K"))
@@ -209,10 +220,11 @@ def write_table(path, results, device, source_hash):
         if str(r["best_tile"]) not in times or str(r.get("current")) not in times:
             times = r["us"]
         best_us = times[str(r["best_tile"])]
+        remap = r.get("remap", 0)
         if r["group_m"]:
-            best_us = r["group_us"][str(r["group_m"])]
+            best_us = r["group_us"][str(r["group_m"]) + ("x" if remap == 2 else "")]
         was = times.get(str(r.get("current")), r["auto_us"])
-        lines.append(f"{{{lm}, {ln}, {lk}, {r['best_tile']}, {r['group_m']}}},"
+        lines.append(f"{{{lm}, {ln}, {lk}, {r['best_tile']}, {r['group_m']}, {remap}}},"
                      f"  // {r['M']}x{r['N']}x{r['K']}: {best_us} (was {was})")
     with open(path, "w") as f:
         f.write("\n".join(lines) + "\n")

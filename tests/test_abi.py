@@ -102,13 +102,13 @@ TUNE_TABLE = os.path.join(ROOT, "dense_gemm_f16f32_amd", "csrc", "tune_table.inc
 
 
 def tune_entries():
-    """(log2 M, log2 N, log2 K) -> (tile, group) rows of the compiled dispatch table."""
+    """(log2 M, log2 N, log2 K) -> (tile, group, remap) rows of the compiled dispatch table."""
     rows = {}
     for ln in open(TUNE_TABLE):
-        m = re.match(r"\s*\{(-?\d+), (-?\d+), (-?\d+), (\d+), (\d+)\}", ln)
+        m = re.match(r"\s*\{(-?\d+), (-?\d+), (-?\d+), (\d+), (\d+), (\d+)\}", ln)
         if m:
-            lm, lnn, lk, tile, grp = map(int, m.groups())
-            rows[(lm, lnn, lk)] = (tile, grp)
+            lm, lnn, lk, tile, grp, remap = map(int, m.groups())
+            rows[(lm, lnn, lk)] = (tile, grp, remap)
     return rows
 
 
@@ -131,12 +131,13 @@ def test_tune_table_rows_are_valid():
 
 
 def test_planner_follows_the_table():
-    for (lm, ln, lk), (tile, grp) in sorted(tune_entries().items()):
+    for (lm, ln, lk), (tile, grp, remap) in sorted(tune_entries().items()):
         M, N, K = 1 << lm, 1 << ln, 1 << lk
         p = plan(M, N, K)
         assert p["tile"] == tile, (M, N, K)
         want_g = grp or plan(M, N, K, tile=tile)["group_m"]
         assert p["group_m"] == want_g, (M, N, K)
+        assert p["xcd_remap"] == (0 if remap == 2 else 1), (M, N, K)
         # a non-power-of-two shape in the same class gets the same tile
         p2 = plan(M + M // 8, N, K)
         if shape_class(M + M // 8, N, K) == (lm, ln, lk) and p2["launches"] == 1:

@@ -14,11 +14,14 @@ def fake_results():
         for M in (32, 4096, 8192):
             for N in (32, 768, 8192):
                 best = g.TILE_256x256x64 if min(M, N) >= 4096 else g.TILE_32x64x64
+                big = best == g.TILE_256x256x64
                 rows.append({"M": M, "N": N, "K": K, "best_tile": best,
-                             "group_m": 4 if best == g.TILE_256x256x64 and K == 4096 else 0,
+                             "group_m": 4 if big and K == 4096 else (1 if big else 0),
+                             "remap": 2 if big and K == 64 else 0,
                              "current": g.TILE_128x64x64,
                              "us": {str(best): 10.0, str(g.TILE_128x64x64): 12.5},
-                             "ab_us": {}, "group_us": {"4": 9.5}, "auto_us": 12.0})
+                             "ab_us": {}, "group_us": {"4": 9.5, "1x": 9.25},
+                             "auto_us": 12.0})
     return rows
 
 
@@ -32,9 +35,10 @@ def test_written_rows_parse_back(tmp_path, monkeypatch):
     assert len(parsed) == len(rows)
     for r in rows:
         key = shape_class(r["M"], r["N"], r["K"])
-        assert parsed[key] == (r["best_tile"], r["group_m"]), r
+        assert parsed[key] == (r["best_tile"], r["group_m"], r["remap"]), r
     text = out.read_text()
     assert "test device" in text and "12.5" in text       # the replaced choice's time
+    assert "9.25" in text                                  # G = 1 with the permutation off
 
 
 def test_keys_are_rounded_log2():
