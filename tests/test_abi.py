@@ -125,8 +125,9 @@ def expected_choice(M, N, K):
 
 def test_tune_table_rows_are_valid():
     rows = tune_entries()
-    for key, (tile, grp) in rows.items():
-        assert tile in g.TILES and 0 <= grp <= 64, key
+    assert len(rows) == 9 * 9 * 8
+    for key, (tile, grp, remap) in rows.items():
+        assert tile in g.TILES and 0 <= grp <= 64 and remap in (0, 2), key
         assert 5 <= key[0] <= 13 and 5 <= key[1] <= 13 and 6 <= key[2] <= 13, key
 
 
@@ -156,7 +157,13 @@ def test_plans_for_the_five_workloads():
     # the pages' worked example, forced: 128 x 64 tiles with G = 2
     p = plan(1024, 768, 128, tile=g.TILE_128x64x64, group_m=2)
     assert (p["num_pid_m"], p["num_pid_n"], p["num_programs"], p["group_m"]) == (8, 12, 96, 2)
-    assert plan(8192, 8192, 8192)["xcd_remap"] == 1
+    # 8192^3 follows the table's order (measured: G = 2 with the XCD permutation off); an
+    # explicit option overrides it
+    want = tune_entries()[shape_class(8192, 8192, 8192)]
+    p = plan(8192, 8192, 8192)
+    assert (p["group_m"] if want[1] else 0, p["xcd_remap"]) == (want[1], 0 if want[2] == 2 else 1)
+    assert plan(8192, 8192, 8192, xcd_remap=g.REMAP_ON)["xcd_remap"] == 1
+    assert plan(8192, 8192, 8192, xcd_remap=g.REMAP_OFF)["xcd_remap"] == 0
     # ragged, 256 x 256 tiles: the 1-column sliver is split off, the main launch covers
     # 4095 x 4096 with 16 x 16 tiles
     p = plan(4095, 4097, 4093, tile=g.TILE_256x256x64, group_m=6, split_edges=g.SPLIT_ON)
