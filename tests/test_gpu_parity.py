@@ -158,7 +158,7 @@ def test_edge_split_changes_no_bit(M, N):
     A, B = operands(M, N, K, "n(0,0.1)", M + N)
     Ad, Bd = to_dev(A), to_dev(B)
     rc, info = g.gemm_f16f32_plan(M, N, K, 1 << 40, 2 << 40, 3 << 40, K, N, N)
-    assert info["launches"] > 1
+    assert info["launches"] > 1 or info["strip_n"] > 0   # split off, or taken into the launch
     split = from_dev(run(Ad, Bd, M, N, K))
     whole = from_dev(run(Ad, Bd, M, N, K, split_edges=g.SPLIT_OFF))
     assert np.array_equal(split, whole)
