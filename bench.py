@@ -462,15 +462,25 @@ def main():
             print(json.dumps(r), file=sys.stderr, flush=True)
 
     if args.sweep:
-        for G in (1, 2, 4, 8, 16, 32):
-            for remap in (1, 2):
+        # interleaved: 4 rounds over all (G, permutation) pairs, alternating direction, each
+        # a block of `steps` event-timed launches; the median of the block medians per pair
+        # (the chip's power state drifts over a sweep)
+        pairs = [(G, remap) for G in (1, 2, 4, 8, 16, 32) for remap in (1, 2)]
+        blocks = {pr: [] for pr in pairs}
+        for rnd in range(4):
+            for G, remap in (pairs if rnd % 2 == 0 else pairs[::-1]):
                 o = dict(opts, group_m=G, xcd_remap=remap)
-                rr = time_workload(g, torch, args.workload, args.steps, args.warmup, o)
-                print(json.dumps({"workload": args.workload, "group_m": G,
-                                  "xcd_remap": remap == 1,
-                                  "tflops": round(rr["achieved_tflops"], 1),
-                                  "kernel_ms_median": round(rr["kernel_ms_median"], 4)}),
-                      file=sys.stderr, flush=True)
+                rr = time_workload(g, torch, args.workload, args.steps,
+                                   args.warmup if rnd == 0 else 2, o)
+                blocks[(G, remap)].append(rr["kernel_ms_median"])
+        _, M, N, K, _, _ = workload(args.workload)
+        for (G, remap), v in blocks.items():
+            med = sorted(v)[len(v) // 2]
+            print(json.dumps({"workload": args.workload, "group_m": G,
+                              "xcd_remap": remap == 1, "rounds": len(v),
+                              "kernel_ms_median": round(med, 4),
+                              "tflops": round(2.0 * M * N * K / (med * 1e-3) / 1e12, 1)}),
+                  file=sys.stderr, flush=True)
     if args.layouts:
         for lay in ("nn", "nt", "tn", "tt", "nnt", "ntt", "tnt", "ttt"):
             rr = time_workload(g, torch, args.workload, args.steps, args.warmup, opts, lay)

@@ -15,19 +15,27 @@ def test_more_than_one_gpu_is_refused():
     assert r.returncode == 2 and "one GPU" in r.stderr and r.stdout == ""
 
 
-def test_traffic_record_matches_current_kernel_source():
+def test_traffic_record_matches_current_kernel_and_plan():
+    """The committed record is for the launch configuration the planner picks at 8192^3 and
+    was taken with the kernels that ship."""
+    import dense_gemm_f16f32_amd as g
     with open(bench.TRAFFIC_FILE) as f:
         rec = json.load(f)
-    e = rec["gemm8192_u/tile1/g8/remap1"]
+    rc, p = g.gemm_f16f32_plan(8192, 8192, 8192, 1 << 40, 2 << 40, 3 << 40, 8192, 8192, 8192)
+    assert rc == g.OK
+    key = f"gemm8192_u/tile{p['tile']}/g{p['group_m']}/remap{p['xcd_remap']}"
+    e = rec[key]
     fetch = e["fetch_size_kib_per_dispatch"] * 1024 * e["fetch_factor"]
     write = e["write_size_kib_per_dispatch"] * 1024 * e["write_factor"]
     assert abs(fetch + write - e["bytes_per_launch"]) < 1e3
     assert e["algorithmic_bytes_per_launch"] == 2 * 3 * 8192 * 8192
-    if e["source_hash"] == bench.kernel_source_hash():
-        assert bench.measured_traffic("gemm8192_u", 1, 8, 1) == e["bytes_per_launch"]
-    # any other launch configuration, or a changed kernel, reports no traffic
-    assert bench.measured_traffic("gemm8192_u", 1, 4, 1) is None
-    assert bench.measured_traffic("gemm4096_u", 1, 8, 1) is None
+    assert e["source_hash"] == bench.kernel_source_hash()
+    assert bench.measured_traffic("gemm8192_u", p["tile"], p["group_m"], p["xcd_remap"]) == \
+        e["bytes_per_launch"]
+    # any other launch configuration reports no traffic
+    assert bench.measured_traffic("gemm8192_u", p["tile"], p["group_m"] + 1,
+                                  p["xcd_remap"]) is None
+    assert bench.measured_traffic("gemm4096_u", p["tile"], p["group_m"], p["xcd_remap"]) is None
 
 
 def test_traffic_is_dropped_when_the_kernel_changes(tmp_path, monkeypatch):
