@@ -4,9 +4,10 @@ The launch grid of a GEMM depends on its tile shape, and which tile (and which g
 is fastest depends on the problem's shape: the tutorial that the grouped order comes from
 leaves the block sizes to an autotuner keyed on M, N and K.  This script is that autotuner,
 run once, offline: for every shape class of a log2 grid it times each tile configuration
-of the library (forced through gemm_f16f32_ex options), then GROUP_SIZE_M in 1..32 for the
-winner when the grid is large enough for the order to matter, and writes the winners as a
-C table (csrc/tune_table.inc) that the library's planner looks up by rounded log2 of
+of the library (forced through gemm_f16f32_ex options), then GROUP_SIZE_M in 1..32 with the
+XCD permutation on and off for the winner when the grid is large enough for the order to
+matter, and writes the winners as a C table (csrc/tune_table.inc, headed by the kernel
+source hash it was measured at) that the library's planner looks up by rounded log2 of
 (M, N, K).
 
 Each timing is the device time per launch of a HIP graph holding n back-to-back launches on
