@@ -173,6 +173,36 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)n, 0x00020000);
 }
 
+// Buffer-resource fields of consecutive panels of one operand, stepped one panel at a time:
+// the byte address of the panel's corner and the bytes from there to one past the matrix's
+// last element, rounded up to a dword (the step is a multiple of 4 bytes, so the rounding
+// stays exact).  Gives the same resource as make_rsrc(corner, bytes) for a live panel, and an
+// empty one (no memory touched, zeros) for a panel past the end.
+struct PanelSeq {
+  uint64_t addr;
+  int64_t rem, step;
+  __device__ __forceinline__ void init(const uint16_t* base, int64_t e0, int64_t ext,
+                                       int64_t step_elems) {
+    addr = (uint64_t)(uintptr_t)base + 2 * (uint64_t)e0;
+    rem = (2 * (ext - e0) + 3) & ~(int64_t)3;
+    step = 2 * step_elems;
+  }
+  // A live panel starts before the matrix's end (rem > 0); more than 4 GiB saturates.  The
+  // high word passes through an empty asm so that the test stays one 32-bit scalar compare
+  // (a 64-bit compare would go to the vector unit).
+  __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(bool live) const {
+    uint32_t hi = (uint32_t)((uint64_t)rem >> 32);
+    asm("" : "+s"(hi));
+    const uint32_t lo = (uint32_t)rem;
+    const uint32_t n = live ? (hi != 0 ? 0xFFFFFFFCu : lo) : 0u;
+    return __builtin_amdgcn_make_buffer_rsrc((void*)addr, (short)0, (int)n, 0x00020000);
+  }
+  __device__ __forceinline__ void next() {
+    addr += (uint64_t)step;
+    rem -= step;
+  }
+};
+
 // 16-byte buffer -> LDS load: lane l's 16 bytes from (resource, voff) land at dst + 16 l.
 // The builtin exists only for the device; in the host pass of this single-source file the
 // call must not appear at all, or the kernels' host launch stubs are not emitted.
@@ -325,8 +355,8 @@ __device__ __forceinline__ void read_frags(Frag<T>& f, const char GK_LDS* st,
 //    states after the tile's last MFMA and only then hands the accumulators back to the
 //    compiler, so no read is scheduled above it.
 //  * An LDS load overwriting an MFMA's A or B operand registers while it may still read them:
-//    the operand ring holds two k steps, and a register is reloaded at the earliest 29 MFMAs
-//    after the last MFMA that read it (see `panel` in dma_tile).
+//    the operand ring holds two k steps, and a register is reloaded at the earliest 8 MFMAs
+//    (over 100 cycles) after the last MFMA that read it (see `panel` in dma_tile).
 //  * MFMA result fed to the next MFMA on the same accumulator (SrcC = vdst, same size): back
 //    to back is allowed; here 63 other MFMAs lie between.
 __device__ __forceinline__ void mfma16(float4v& acc, const half8& a, const half8& b) {
@@ -738,6 +768,22 @@ __device__ __forceinline__ void dma_tile(const Args& p, int m0, int n0,
   // Operands are read RD k steps ahead of the MFMAs that use them: a ring of RD + 1
   // fragments, indexed by the k step's position in the NS-panel unrolled loop.
   Frag<T> f[RD + 1];
+  // Tile 1 (16x16x32 MFMAs, NS == 2): the refill resources of panel s+2, stepped once per
+  // panel rather than recomputed from the panel index next to the barrier, where the matrix
+  // core would wait for the scalar work; B's resource is kept for the second half of its
+  // slots, issued in the next panel's first k step.
+  static_assert(!T::M16 || (NS == 2 && kSplitRefill), "16x16x32 schedule");
+  // Panel 1 is loaded before the loop except for that second half of B's slots, which panel
+  // 0's first k step issues like every other panel's (so that step has no branch).
+  PanelSeq qa{}, qb{};
+  if constexpr (T::M16) {
+    const int64_t k1 = (int64_t)kofs + BK, k2 = k1 + BK;
+    qa.init(p.A, elem_off<OA::KM>(m0, k2, p.lda), extA, OA::KM ? BK : (int64_t)BK * p.lda);
+    qb.init(p.B, elem_off<OB::KM>(n0, k1, p.ldb), extB, OB::KM ? BK : (int64_t)BK * p.ldb);
+  }
+  __amdgpu_buffer_rsrc_t rb_half = qb.rsrc(1 < np);
+  qb.next();
+  __amdgpu_buffer_rsrc_t ra_nx = rb_half, rb_nx = rb_half;   // panel s+2's, from step 0 on
 
   // Panel s from stage `cur` (position j in the unrolled loop), with panel s+1 in `nxt`;
   // `prev` held panel s-1.  K step kk multiplies the operands of step kk and reads those of
@@ -776,27 +822,28 @@ __device__ __forceinline__ void dma_tile(const Args& p, int m0, int n0,
       const int ka = kk + RD;
       if constexpr (T::M16) {
         // Scheduled by hand (the MFMAs are asm, which the scheduling hints do not see): one
-        // operand read of the next k step, and at most one refill load, after every fourth of
-        // the step's 64 MFMAs.
+        // operand read of the next k step after every fourth of the step's 64 MFMAs, the B
+        // fragments first (the next step's first 8 MFMAs need all of them and A's first), and
+        // the refill loads in between.
         const char GK_LDS* src = ka < KS ? cur : nxt;
         const int kr = ka < KS ? ka : ka - KS;
         Frag<T>& nf = f[(j * KS + ka) % (RD + 1)];
         const Frag<T>& cf = f[(j * KS + kk) % (RD + 1)];
         // refill loads of this step: at the barrier step slots [0, A_LD + B_LD/2) of panel
-        // s+2 into `cur`; at the first step the other half of B's slots of panel s+1 (into nxt)
-        const bool bar = kk == KS - RD, spl = kSplitRefill && kk == 0 && s > 0;
-        const int sp = bar ? s + NS : s + 1;
-        const bool live = sp < np;
-        const int64_t k0 = (int64_t)kofs + (int64_t)sp * BK;
-        const int64_t eA = elem_off<OA::KM>(m0, k0, p.lda), eB = elem_off<OB::KM>(n0, k0, p.ldb);
-        const __amdgpu_buffer_rsrc_t rA = make_rsrc(p.A + (live ? eA : 0), live ? 2 * (extA - eA) : 0);
-        const __amdgpu_buffer_rsrc_t rB = make_rsrc(p.B + (live ? eB : 0), live ? 2 * (extB - eB) : 0);
+        // s+2 into `cur`; at the first step the other half of B's slots of panel s+1 (into
+        // nxt; for panel 0 too, see rb_half)
+        const bool bar = kk == KS - RD, spl = kk == 0;
+        const __amdgpu_buffer_rsrc_t rA = ra_nx, rB = bar ? rb_nx : rb_half;
         char GK_LDS* dA = bar ? cur : nxt;
         char GK_LDS* dB = dA + T::A_BYTES;
 #pragma unroll
         for (int i = 0; i < T::TM * T::TN; ++i) {
-          if (i % 4 == 2) {
-            const int q = i / 4;
+          // refill loads: the barrier step's 12 every kBarGap MFMAs from MFMA kBarAt on, the
+          // first step's 4 every kSplGap from MFMA kSplAt on
+          constexpr int kBarGap = 4, kSplGap = 4, kBarAt = 2, kSplAt = 2;
+          const int gap = bar ? kBarGap : kSplGap, at = bar ? kBarAt : kSplAt;
+          if (i >= at && (i - at) % gap == 0) {
+            const int q = (i - at) / gap;
             if (bar) {
               if (q < T::A_LD)
                 buffer_load_lds16(rA, (void GK_LDS*)(dA + (q * OA::NW + w) * 1024), offA[q]);
@@ -811,14 +858,30 @@ __device__ __forceinline__ void dma_tile(const Args& p, int m0, int n0,
           }
           const int tm = i / T::TN, tn = i % T::TN;
           mfma16(acc[tm][tn], cf.a[tm], cf.b[tn]);
+          // The resources of panel s+2, for the barrier step's refill: A's after MFMA 16 of
+          // the first step, B's after MFMA 20.  The empty asms keep each piece of scalar work
+          // between two MFMAs (away from the barrier, where it would delay the next MFMA, and
+          // not in one cluster).
+          if (spl && i == 16) {
+            asm volatile("" : "+s"(qa.addr), "+s"(qa.rem));
+            ra_nx = qa.rsrc(s + NS < np);
+            qa.next();
+          }
+          if (spl && i == 20) {
+            asm volatile("" : "+s"(ra_nx), "+s"(qb.addr), "+s"(qb.rem));
+            rb_nx = qb.rsrc(s + NS < np);
+            qb.next();
+          }
+          if (spl && i == 24) asm volatile("" : "+s"(rb_nx));
           if (i % 4 == 0 && i / 4 < T::TM + T::TN) {
             const int r = i / 4;
-            if (r < T::TM)
-              nf.a[r] = read_operand<typename T::OA>(src, lo.a, r, kr);
+            if (r < T::TN)
+              nf.b[r] = read_operand<typename T::OB>(src, lo.b, r, kr);
             else
-              nf.b[r - T::TM] = read_operand<typename T::OB>(src, lo.b, r - T::TM, kr);
+              nf.a[r - T::TN] = read_operand<typename T::OA>(src, lo.a, r - T::TN, kr);
           }
         }
+        if (bar) rb_half = rb_nx;
       } else {
         if (ka < KS)
           read_frags<T>(f[(j * KS + ka) % (RD + 1)], cur, lo, ka);
@@ -857,9 +920,14 @@ __device__ __forceinline__ void dma_tile(const Args& p, int m0, int n0,
       head(S[0]);
     else
       issue(0, S[0]);
+    if constexpr (T::M16) {
+      issue(1, S[1], 1);   // the rest in panel 0's first k step
+      wait_vmcnt<T::A_LD + kBHalf>();
+    } else {
 #pragma unroll
-    for (int j = 1; j < kPre; ++j) issue(j, S[j]);
-    wait_vmcnt<(kPre - 1) * NV>();
+      for (int j = 1; j < kPre; ++j) issue(j, S[j]);
+      wait_vmcnt<(kPre - 1) * NV>();
+    }
     if (has_last && np == 1) patch(S[0]);
     lds_barrier();
 #pragma unroll

@@ -142,9 +142,10 @@ def tune_shape(torch, M, N, K, quick=False):
     elif current in times and times[best] > (1.0 - MARGIN) * times[current]:
         best = current
     # GROUP_SIZE_M and the XCD permutation (on: key "G", off: key "Gx"), for grids large
-    # enough for the order to matter; the tile's default (its G, permutation on) stays unless
-    # another order is clearly faster in interleaved rounds
-    group, remap, group_times = 0, 0, {}
+    # enough for the order to matter: two passes over the 12 orders, then interleaved rounds
+    # among the closest; the tile's default (its G, permutation on) stays unless another
+    # order is clearly faster in those rounds
+    group, remap, group_times, group_ab = 0, 0, {}, {}
     if programs(M, N, best) >= 128:
         rc, info = g.gemm_f16f32_plan(M, N, K, A.data_ptr(), B.data_ptr(), C.data_ptr(), K, N,
                                       N, opts=dict(tile=best))
@@ -159,14 +160,28 @@ def tune_shape(torch, M, N, K, quick=False):
                 runs[k].append(graph_time_us(torch, fns[k], target_us=1500.0))
         group_times = {k: sum(v) / len(v) for k, v in runs.items()}
         gbest = min(group_times, key=group_times.get)
-        if gbest != default_key and \
-                group_times[gbest] < (1.0 - MARGIN) * group_times[default_key]:
-            group, remap = int(gbest.rstrip("x")), (2 if gbest.endswith("x") else 0)
+        # As for the tiles: orders within CLOSE of the fastest (and the default) are re-timed
+        # in interleaved rounds; the default stays unless another is AB_MARGIN faster there.
+        close = [k for k in sorted(group_times, key=group_times.get)
+                 if group_times[k] <= (1 + CLOSE) * group_times[gbest]][:4]
+        if default_key not in close:
+            close.append(default_key)
+        if len(close) > 1:
+            gruns = {k: [] for k in close}
+            for r in range(AB_ROUNDS):
+                for k in close[r % len(close):] + close[:r % len(close)]:
+                    gruns[k].append(graph_time_us(torch, fns[k], target_us=1500.0))
+            group_ab = {k: sorted(v)[len(v) // 2] for k, v in gruns.items()}
+            gbest = min(group_ab, key=group_ab.get)
+            if gbest != default_key and \
+                    group_ab[gbest] < (1.0 - AB_MARGIN) * group_ab[default_key]:
+                group, remap = int(gbest.rstrip("x")), (2 if gbest.endswith("x") else 0)
     return {"M": M, "N": N, "K": K, "best_tile": best, "group_m": group, "remap": remap,
             "current": current,
             "us": {str(k): round(v, 2) for k, v in times.items()},
             "ab_us": {str(k): round(v, 2) for k, v in ab.items()},
             "group_us": {str(k): round(v, 2) for k, v in group_times.items()},
+            "group_ab_us": {str(k): round(v, 2) for k, v in group_ab.items()},
             "auto_us": round(auto, 2)}
 
 
