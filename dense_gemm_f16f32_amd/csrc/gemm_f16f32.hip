@@ -70,13 +70,8 @@ struct Choice {
 };
 
 // Tile and group size for an M x N x K launch: the table's entry for its shape class, else
-// the heuristic with the tile's default group size.  The table was measured on 16-byte
-// aligned rows; when some rows of an operand are not (an odd leading dimension, a 2-byte
-// aligned start), a 16-byte load of a panel row straddles one more cache line, the fetch
-// takes longer, and two wavefronts per SIMD hide it better: there the 8-wavefront ping-pong
-// tile replaces the 4-wavefront 256 x 256 one (measured 6 % faster on 4095 x 4097 x 4093 and
-// 9 % on 4096^3 with odd leading dimensions, level at 8192^3).
-Choice choose_tile(int64_t M, int64_t N, int64_t K, bool aligned) {
+// the heuristic with the tile's default group size.
+Choice choose_tile(int64_t M, int64_t N, int64_t K) {
   const int lm = log2_class(M, 5, 13), ln = log2_class(N, 5, 13), lk = log2_class(K, 6, 13);
   Choice c = {heuristic_tile(M, N), 0, 0};
   for (const TuneEntry& e : kTune)
@@ -84,7 +79,6 @@ Choice choose_tile(int64_t M, int64_t N, int64_t K, bool aligned) {
       c = {e.tile, e.group, e.remap};
       break;
     }
-  if (!aligned && c.tile == GEMM_F16F32_TILE_256x256x64) c.tile = GEMM_F16F32_TILE_256x256x32_PP;
   return c;
 }
 
@@ -167,11 +161,11 @@ bool aligned_rows(const Problem& pr) {
 // at least 512 deep; two slices paid off only from K = 4096 on (the reduction's launch and
 // fp32 traffic cost about 1-2 us).  So: the largest power of two S <= 16 with that grid
 // within 256 and K >= 512 S, and S = 2 only for K >= 4096.
-int auto_splits(int64_t M, int64_t N, int64_t K, int tile, bool aligned) {
+int auto_splits(int64_t M, int64_t N, int64_t K, int tile) {
   int best = 1;
   for (int S = 2; S <= 16 && K >= 512 * (int64_t)S; S *= 2) {
     const int64_t L = cdiv(cdiv(K, S), 128) * 128;
-    const TileDesc* t = find_tile(tile ? tile : choose_tile(M, N, L, aligned).tile);
+    const TileDesc* t = find_tile(tile ? tile : choose_tile(M, N, L).tile);
     if (cdiv(M, t->bm) * cdiv(N, t->bn) * S <= kCUs) best = S;
   }
   return (best == 2 && K < 4096) ? 1 : best;
@@ -292,7 +286,7 @@ int plan_parts(const Problem& pr, const gemm_f16f32_opts* opts, int64_t ws_bytes
     return GEMM_F16F32_ERR_OPTS;
   if (o.split_k == GEMM_F16F32_SPLIT_K_AUTO) {
     const bool may = ws_bytes > 0 && !emptyC && o.force_generic != 1 && o.persistent != 1;
-    const int S = may ? auto_splits(M, N, K, o.tile, aligned_rows(pr)) : 1;
+    const int S = may ? auto_splits(M, N, K, o.tile) : 1;
     if (S > 1) {
       gemm_f16f32_opts os = o;
       os.split_k = S;
@@ -315,13 +309,24 @@ int plan_parts(const Problem& pr, const gemm_f16f32_opts* opts, int64_t ws_bytes
       return GEMM_F16F32_ERR_OVERLAP;
   }
 
-  const bool aligned = aligned_rows(pr);
   // A split problem is chosen for as the slices' own shape, M x N x L.
-  const Choice ch = o.tile ? Choice{o.tile, 0, 0} : choose_tile(M, N, split_k ? L : K, aligned);
-  const TileDesc* t = find_tile(ch.tile);
-  int64_t Mm = M, Nm = N;
+  Choice ch = o.tile ? Choice{o.tile, 0, 0} : choose_tile(M, N, split_k ? L : K);
   const bool split =
       !split_k && (o.split_edges == 1 || (o.split_edges == 0 && o.tile == 0));
+  // A right sliver of 1..16 columns with misaligned rows (an odd leading dimension or a 2-byte
+  // aligned start, where a 16-byte load of a panel row straddles one more cache line): where
+  // the table picks the 256 x 256 x 64 tile, the ping-pong tile of the same size computes the
+  // sliver inside its own launch instead of a second launch (measured on 4095 x 4097 x 4093:
+  // 144 against 152 us).  Without such a sliver misaligned rows keep the table's tile.
+  if (o.tile == 0 && split && !emptyC && ch.tile == GEMM_F16F32_TILE_256x256x64 &&
+      !aligned_rows(pr) && o.force_generic != 1 && o.persistent != 1) {
+    const int64_t rn = N % 256, rm = M % 256, fm = M / 256, fn = N / 256;
+    const bool bottom = fm * fn >= 128 && rm > 0 && 4 * rm <= 256;
+    if (rn > 0 && rn <= 16 && fn >= 16 && !bottom)
+      ch = Choice{GEMM_F16F32_TILE_256x256x32_PP, 0, 0};
+  }
+  const TileDesc* t = find_tile(ch.tile);
+  int64_t Mm = M, Nm = N;
   int64_t strip_n = 0;
   if (split && !emptyC) {
     const int64_t rm = M % t->bm, rn = N % t->bn;
@@ -371,7 +376,7 @@ int plan_parts(const Problem& pr, const gemm_f16f32_opts* opts, int64_t ws_bytes
   for (const auto& st : strips) {
     if (st[2] == 0 || st[3] == 0) continue;
     pp->m_off = st[0], pp->n_off = st[1], pp->M = st[2], pp->N = st[3];
-    const Choice cs = choose_tile(st[2], st[3], K, aligned);
+    const Choice cs = choose_tile(st[2], st[3], K);
     rc = plan_or_fallback(st[2], st[3], find_tile(cs.tile), cs.group, cs.remap, false, os, &pp->r);
     if (rc != GEMM_F16F32_OK) return rc;
     ++pp;

@@ -948,14 +948,197 @@ __device__ __forceinline__ void dma_tile(const Args& p, int m0, int n0,
     store_tile<T>(p, acc, m0, n0, wm, wn, lane);
 }
 
+// ---------------------------------------------------------------------------------------
+// The 256 x 256 x 64 tile on 16x16x32 MFMAs, one workgroup per program: the operand panels
+// in five LDS slots of 32 KiB (all 160 KiB), A's in a ring of three and B's in a ring of two.
+// With two 64 KiB stages a panel's whole refill can only start at the barrier that frees its
+// stage; here A of panel s+2 goes to the slot that held A of panel s-1 -- free since panel
+// s-1's barrier -- and is loaded during panel s's first k step, and B of panel s+2 goes to
+// B's slot of panel s after panel s's barrier.  Each k step then issues 8 loads per wave,
+// one every 8 MFMAs, instead of 12 in one step and 4 in the other, and A's loads have two k
+// steps to land.  Per panel s:
+//   first k step:  MFMAs of step 0 (operands in registers), reads of step 1's operands from
+//                  panel s's slots, A of panel s+2 loaded; B's resource of panel s+2 computed.
+//   barrier:       this wave's loads of panel s+1 have landed (only A of panel s+2 may be in
+//                  flight), then every wave's.
+//   second k step: MFMAs of step 1, reads of panel s+1's step 0 operands, B of panel s+2
+//                  loaded; A's resource of panel s+3 computed.
+// Slot indices repeat every 6 panels, so the loop is unrolled by 6 and leaves after the last
+// panel.  The k order of every element's sum is the one of the other schedules: same bits.
+// ---------------------------------------------------------------------------------------
+template <bool AKM, bool BKM>
+__device__ __forceinline__ void ring_tile(const Args& p, int m0, int n0,
+                                          char GK_LDS* const (&SA)[3],
+                                          char GK_LDS* const (&SB)[2]) {
+  using T = Tile<256, 256, 64, AKM, BKM, 2, 2>;
+  using OA = typename T::OA;
+  using OB = typename T::OB;
+  constexpr int BK = 64;
+  static_assert(T::M16 && OA::BYTES == 32768 && OB::BYTES == 32768 && T::A_LD == 8 &&
+                T::B_LD == 8 && T::TM == 8 && T::TN == 8, "ring tile shape");
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = w / 2, wn = w % 2;
+  uint32_t offA[T::A_LD], offB[T::B_LD];
+  slot_offsets<OA>(offA, w, lane, p.lda);
+  slot_offsets<OB>(offB, w, lane, p.ldb);
+  const int64_t extA = extent<AKM>(p.M, p.K, p.lda);
+  const int64_t extB = extent<BKM>(p.N, p.K, p.ldb);
+  const int rk = p.K % BK;                    // depth of the head panel (0: none)
+  const int np = p.K / BK + (rk ? 1 : 0);
+  const int kofs = rk ? rk - BK : 0;          // panel s covers k in [kofs + s BK, + BK)
+  uint16_t last_a = 0, last_b = 0;
+  const int patch_a = last_element_slot<OA>(m0, p.M, p.K, p.A, extA, tid, last_a);
+  const int patch_b = last_element_slot<OB>(n0, p.N, p.K, p.B, extB, tid, last_b);
+  auto patch = [&](char GK_LDS* a, char GK_LDS* b) __attribute__((always_inline)) {
+    if (patch_a >= 0) *(uint16_t GK_LDS*)(a + patch_a) = last_a;
+    if (patch_b >= 0) *(uint16_t GK_LDS*)(b + patch_b) = last_b;
+  };
+
+  typename T::Acc acc[T::TM][T::TN];
+#pragma unroll
+  for (int tm = 0; tm < T::TM; ++tm)
+#pragma unroll
+    for (int tn = 0; tn < T::TN; ++tn) acc[tm][tn] = typename T::Acc{};
+  mfma16_pin_zero<T>(acc);
+
+  int oa[OA::NOFF], ob[OB::NOFF];   // per-lane read offsets inside a slot
+  operand_offsets<OA>(oa, wm, lane, 0);
+  operand_offsets<OB>(ob, wn, lane, 0);
+  Frag<T> f[2];                     // f[0]: step 0's operands, f[1]: step 1's
+
+  // refill resources: A's of panel s+2 (s+3 once stepped in the second k step), B's of s+2
+  PanelSeq qa{}, qb{};
+  {
+    const int64_t k2 = (int64_t)kofs + 2 * BK;
+    qa.init(p.A, elem_off<OA::KM>(m0, k2, p.lda), extA, OA::KM ? BK : (int64_t)BK * p.lda);
+    qb.init(p.B, elem_off<OB::KM>(n0, k2, p.ldb), extB, OB::KM ? BK : (int64_t)BK * p.ldb);
+  }
+  __amdgpu_buffer_rsrc_t ra = qa.rsrc(2 < np), rb = ra;
+  qa.next();
+
+  if (np > 0) {
+    if (rk) {
+      u32x4 va[T::A_LD], vb[T::B_LD];
+      head_load<OA>(va, p.A, p.lda, extA, m0, kofs, w, lane);
+      head_load<OB>(vb, p.B, p.ldb, extB, n0, kofs, w, lane);
+      head_store<OA>(va, SA[0], w, lane);
+      head_store<OB>(vb, SB[0], w, lane);
+    } else {
+      dma_panel<OA>(p.A, p.lda, extA, m0, kofs, true, offA, SA[0], w);
+      dma_panel<OB>(p.B, p.ldb, extB, n0, kofs, true, offB, SB[0], w);
+    }
+    const int64_t k1 = (int64_t)kofs + BK;
+    dma_panel<OA>(p.A, p.lda, extA, m0, k1, 1 < np, offA, SA[1], w);
+    dma_panel<OB>(p.B, p.ldb, extB, n0, k1, 1 < np, offB, SB[1], w);
+    wait_vmcnt<T::A_LD + T::B_LD>();   // panel 0 has landed
+    if (np == 1) patch(SA[0], SB[0]);
+    lds_barrier();
+#pragma unroll
+    for (int t = 0; t < T::TN; ++t) f[0].b[t] = read_operand<OB>(SB[0], ob, t, 0);
+#pragma unroll
+    for (int t = 0; t < T::TM; ++t) f[0].a[t] = read_operand<OA>(SA[0], oa, t, 0);
+  }
+
+  // Panel s at position j of the unrolled loop: A in SA[j % 3], B in SB[j % 2].  Each k step
+  // is scheduled by hand (the MFMAs are asm): one operand read of the next step after every
+  // fourth MFMA, B fragments first, and one refill load every 8 MFMAs from MFMA 2 on.
+  auto panel = [&](int s, int j) __attribute__((always_inline)) {
+    char GK_LDS* const a_cur = SA[j % 3];
+    char GK_LDS* const b_cur = SB[j % 2];
+    char GK_LDS* const a_nxt = SA[(j + 1) % 3];
+    char GK_LDS* const b_nxt = SB[(j + 1) % 2];
+    char GK_LDS* const a_new = SA[(j + 2) % 3];   // A of panel s+2 (held A of panel s-1)
+#pragma unroll
+    for (int i = 0; i < 64; ++i) {
+      if (i >= 2 && (i - 2) % 8 == 0) {
+        const int q = (i - 2) / 8;
+        buffer_load_lds16(ra, (void GK_LDS*)(a_new + (q * OA::NW + w) * 1024), offA[q]);
+      }
+      mfma16(acc[i / 8][i % 8], f[0].a[i / 8], f[0].b[i % 8]);
+      // B's resource of panel s+2; the empty asms keep this scalar work between MFMAs 16
+      // and 24, where the matrix core has queued work, rather than next to the barrier
+      if (i == 16) {
+        asm volatile("" : "+s"(qb.addr), "+s"(qb.rem));
+        rb = qb.rsrc(s + 2 < np);
+        qb.next();
+      }
+      if (i == 24) asm volatile("" : "+s"(rb));
+      if (i % 4 == 0) {
+        const int r = i / 4;
+        if (r < 8)
+          f[1].b[r] = read_operand<OB>(b_cur, ob, r, 1);
+        else
+          f[1].a[r - 8] = read_operand<OA>(a_cur, oa, r - 8, 1);
+      }
+    }
+    wait_vmcnt<T::A_LD>();   // panel s+1 has landed (this wave's part) ...
+    if (s + 2 == np) patch(a_nxt, b_nxt);   // panel s+1 is the last one
+    lds_barrier();           // ... every wave's part; and every wave has read B of panel s
+#pragma unroll
+    for (int i = 0; i < 64; ++i) {
+      if (i >= 2 && (i - 2) % 8 == 0) {
+        const int q = (i - 2) / 8;
+        buffer_load_lds16(rb, (void GK_LDS*)(b_cur + (q * OB::NW + w) * 1024), offB[q]);
+      }
+      mfma16(acc[i / 8][i % 8], f[1].a[i / 8], f[1].b[i % 8]);
+      if (i == 16) {   // A's resource of panel s+3, for the next panel's first k step
+        asm volatile("" : "+s"(qa.addr), "+s"(qa.rem));
+        ra = qa.rsrc(s + 3 < np);
+        qa.next();
+      }
+      if (i == 24) asm volatile("" : "+s"(ra));
+      if (i % 4 == 0) {
+        const int r = i / 4;
+        if (r < 8)
+          f[0].b[r] = read_operand<OB>(b_nxt, ob, r, 0);
+        else
+          f[0].a[r - 8] = read_operand<OA>(a_nxt, oa, r - 8, 0);
+      }
+    }
+  };
+  for (int s = 0; s < np; s += 6) {
+#pragma unroll
+    for (int j = 0; j < 6; ++j) {
+      if (s + j >= np) break;
+      panel(s + j, j);
+    }
+  }
+  // The last refills (of panels past the end: empty resources) must land before the
+  // workgroup's LDS is freed.
+  wait_vmcnt<0>();
+  mfma16_drain<T>(acc);
+  store_tile<T>(p, acc, m0, n0, wm, wn, lane);
+}
+
 // One workgroup per program: hardware id -> program id -> tile.
 template <int BM, int BN, int BK, int NS, int RD, int WM, int WN, bool AKM, bool BKM>
 __global__ void __launch_bounds__(64 * WM * WN) gemm_dma(Args p) {
-  GK_DECLARE_STAGES(NS, (Tile<BM, BN, BK, AKM, BKM, WM, WN>::STAGE))
   int pid, pid_m, pid_n;
   program_tile(blockIdx.x, p.num_programs, p.num_pid_m, p.num_pid_n, p.group_m, p.xcd_remap,
                pid, pid_m, pid_n);
-  dma_tile<BM, BN, BK, NS, RD, WM, WN, AKM, BKM>(p, pid_m * BM, pid_n * BN, S);
+  if constexpr (Tile<BM, BN, BK, AKM, BKM, WM, WN>::M16 && NS == 2) {
+    // five separate LDS objects (see ring_tile); their pointers are assigned one by one, as
+    // an initializer list of LDS addresses would become a static table
+    __shared__ __attribute__((aligned(16))) char slot0[32768];
+    __shared__ __attribute__((aligned(16))) char slot1[32768];
+    __shared__ __attribute__((aligned(16))) char slot2[32768];
+    __shared__ __attribute__((aligned(16))) char slot3[32768];
+    __shared__ __attribute__((aligned(16))) char slot4[32768];
+    char GK_LDS* SA[3];
+    char GK_LDS* SB[2];
+    SA[0] = (char GK_LDS*)slot2;
+    SA[1] = (char GK_LDS*)slot3;
+    SA[2] = (char GK_LDS*)slot4;
+    SB[0] = (char GK_LDS*)slot0;
+    SB[1] = (char GK_LDS*)slot1;
+    ring_tile<AKM, BKM>(p, pid_m * BM, pid_n * BN, SA, SB);
+  } else {
+    GK_DECLARE_STAGES(NS, (Tile<BM, BN, BK, AKM, BKM, WM, WN>::STAGE))
+    dma_tile<BM, BN, BK, NS, RD, WM, WN, AKM, BKM>(p, pid_m * BM, pid_n * BN, S);
+  }
 }
 
 // Persistent grouped schedule: a grid of G workgroups (a multiple of 8, at most the number

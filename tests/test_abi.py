@@ -346,18 +346,23 @@ def test_persistent_plans():
         g.ERR_OPTS
 
 
-def test_misaligned_rows_take_the_ping_pong_tile():
-    """Where the table picks the 4-wavefront 256 x 256 tile for aligned rows, misaligned rows
-    (odd leading dimension or a 2-byte aligned start) get the 8-wavefront ping-pong one."""
+def test_misaligned_rows_keep_the_table_tile_unless_a_sliver_fits_the_ping_pong_strip():
+    """Misaligned rows (odd leading dimension or a 2-byte aligned start) keep the table's
+    4-wavefront 256 x 256 tile; only a right sliver of 1..16 columns moves such a problem to the
+    ping-pong tile, which computes the sliver inside its own launch."""
     M = N = K = 4096
     p = plan(M, N, K)
     if p["tile"] != g.TILE_256x256x64:
         pytest.skip("the table does not pick the 4-wavefront 256 x 256 tile here")
-    assert plan(M, N, K, lda=K + 1)["tile"] == g.TILE_256x256x32_PP
-    assert plan(M, N, K, ldb=N + 1)["tile"] == g.TILE_256x256x32_PP
-    assert plan(M, N, K, a=PA + 2)["tile"] == g.TILE_256x256x32_PP
-    assert plan(M, N, K, lda=K + 8)["tile"] == g.TILE_256x256x64
-    assert plan(4095, 4097, 4093)["tile"] == g.TILE_256x256x32_PP
+    for kw in ({"lda": K + 1}, {"ldb": N + 1}, {"a": PA + 2}, {"lda": K + 8}):
+        assert plan(M, N, K, **kw)["tile"] == g.TILE_256x256x64, kw
+    p = plan(4095, 4097, 4093)
+    assert p["tile"] == g.TILE_256x256x32_PP and p["strip_n"] == 1 and p["launches"] == 1
+    # a wider sliver (17 columns) is split off instead, with the table's tile
+    p = plan(4095, 4096 + 17, 4093)
+    assert p["tile"] == g.TILE_256x256x64 and p["strip_n"] == 0 and p["launches"] == 2
+    # the option to force a tile, or to keep the edges, leaves the choice alone
+    assert plan(4095, 4097, 4093, split_edges=g.SPLIT_OFF)["tile"] == g.TILE_256x256x64
 
 
 def test_struct_layouts_match_the_header(tmp_path):
