@@ -38,6 +38,14 @@ const TileDesc* find_tile(int id) {
 
 int64_t cdiv(int64_t x, int64_t y) { return (x + y - 1) / y; }
 
+// LDS bytes of a tile's DMA kernels: its stages of A and B panels, or, for the 256 x 256 x 64
+// tile on 2 x 2 wavefronts, the five 32 KiB panel slots its kernels keep instead.
+int64_t dma_lds_bytes(const TileDesc* t) {
+  if (t->bm == 256 && t->bn == 256 && t->bk == 64 && t->stages == 2 && t->wm == 2 && t->wn == 2)
+    return 5 * 32768;
+  return (int64_t)t->stages * (t->bm + t->bn) * t->bk * 2;
+}
+
 // Tile chosen from the shape when no table entry applies: the largest tile whose grid still
 // covers the 256 CUs about once; smaller problems fall back to smaller tiles so that more CUs
 // take part.  Thin shapes (a side of at most 64) are latency bound over their whole K and
@@ -209,7 +217,7 @@ int plan_launch(const Problem& pr, int64_t M, int64_t N, const TileDesc* t, int 
   r->persistent = dma && o.persistent == 1 && P > 0;
   r->grid = (int32_t)P;
   if (r->persistent) {
-    const int64_t lds = (int64_t)t->stages * (t->bm + t->bn) * t->bk * 2;
+    const int64_t lds = dma_lds_bytes(t);
     const int64_t per_cu = lds > 0 ? (160 * 1024) / lds : 1;
     int64_t g = (int64_t)kCUs * (per_cu > 1 ? per_cu : 1);
     g -= g % 8;

@@ -132,9 +132,9 @@ struct Opnd {
 template <int BM_, int BN_, int BK_, bool AKM, bool BKM, int WM_, int WN_>
 struct Tile {
   static constexpr int WM = WM_, WN = WN_, NW = WM * WN, NT = 64 * NW;  // waves, threads
-  // The 256 x 256 x 64 tile on 2 x 2 wavefronts issues 16x16x32 MFMAs (see `panel` in
-  // dma_tile): on random operands that instruction does more work per joule, and large GEMMs
-  // run at the board's power cap.  Every other tile keeps 32x32x16.
+  // The 256 x 256 x 64 tile on 2 x 2 wavefronts issues 16x16x32 MFMAs (see ring_tile and,
+  // for its generic form, gemm_generic): on random operands that instruction does more work
+  // per joule, and large GEMMs run at the board's power cap.  Every other tile keeps 32x32x16.
   static constexpr bool M16 = BM_ == 256 && BN_ == 256 && BK_ == 64 && WM_ == 2 && WN_ == 2;
   static constexpr int XB = M16 ? 16 : 32, KD = M16 ? 32 : 16, VN = M16 ? 4 : 16;
   using Acc = std::conditional_t<M16, float4v, float16v>;
@@ -356,7 +356,7 @@ __device__ __forceinline__ void read_frags(Frag<T>& f, const char GK_LDS* st,
 //    compiler, so no read is scheduled above it.
 //  * An LDS load overwriting an MFMA's A or B operand registers while it may still read them:
 //    the operand ring holds two k steps, and a register is reloaded at the earliest 8 MFMAs
-//    (over 100 cycles) after the last MFMA that read it (see `panel` in dma_tile).
+//    (over 100 cycles) after the last MFMA that read it (see `panel` in ring_tile).
 //  * MFMA result fed to the next MFMA on the same accumulator (SrcC = vdst, same size): back
 //    to back is allowed; here 63 other MFMAs lie between.
 __device__ __forceinline__ void mfma16(float4v& acc, const half8& a, const half8& b) {
@@ -762,28 +762,12 @@ __device__ __forceinline__ void dma_tile(const Args& p, int m0, int n0,
 #pragma unroll
     for (int tn = 0; tn < T::TN; ++tn)
       acc[tm][tn] = typename T::Acc{};
-  if constexpr (T::M16) mfma16_pin_zero<T>(acc);
 
   const LaneOffsets<T> lo = lane_offsets<T>(wm, wn, lane);
   // Operands are read RD k steps ahead of the MFMAs that use them: a ring of RD + 1
   // fragments, indexed by the k step's position in the NS-panel unrolled loop.
   Frag<T> f[RD + 1];
-  // Tile 1 (16x16x32 MFMAs, NS == 2): the refill resources of panel s+2, stepped once per
-  // panel rather than recomputed from the panel index next to the barrier, where the matrix
-  // core would wait for the scalar work; B's resource is kept for the second half of its
-  // slots, issued in the next panel's first k step.
-  static_assert(!T::M16 || (NS == 2 && kSplitRefill), "16x16x32 schedule");
-  // Panel 1 is loaded before the loop except for that second half of B's slots, which panel
-  // 0's first k step issues like every other panel's (so that step has no branch).
-  PanelSeq qa{}, qb{};
-  if constexpr (T::M16) {
-    const int64_t k1 = (int64_t)kofs + BK, k2 = k1 + BK;
-    qa.init(p.A, elem_off<OA::KM>(m0, k2, p.lda), extA, OA::KM ? BK : (int64_t)BK * p.lda);
-    qb.init(p.B, elem_off<OB::KM>(n0, k1, p.ldb), extB, OB::KM ? BK : (int64_t)BK * p.ldb);
-  }
-  __amdgpu_buffer_rsrc_t rb_half = qb.rsrc(1 < np);
-  qb.next();
-  __amdgpu_buffer_rsrc_t ra_nx = rb_half, rb_nx = rb_half;   // panel s+2's, from step 0 on
+  static_assert(!T::M16, "the 16x16x32 tile runs on ring_tile");
 
   // Panel s from stage `cur` (position j in the unrolled loop), with panel s+1 in `nxt`;
   // `prev` held panel s-1.  K step kk multiplies the operands of step kk and reads those of
@@ -811,87 +795,21 @@ __device__ __forceinline__ void dma_tile(const Args& p, int m0, int n0,
       if constexpr (kSplitRefill) {
         // the rest of panel s+1's refill, started at the previous panel's barrier (panel 1 was
         // loaded whole before the loop)
-        if (!T::M16 && kk == 0 && s > 0) issue(s + 1, nxt, 2);
+        if (kk == 0 && s > 0) issue(s + 1, nxt, 2);
       }
       if (kk == KS - RD) {
         wait_vmcnt<(NS - 2) * NV>();   // panel s+1 has landed (this wave's part)
         if (has_last && s + 2 == np) patch(nxt);   // panel s+1 is the last one
         lds_barrier();                 // ... every wave's part
-        if constexpr (NS == 2 && !T::M16) issue(s + NS, cur, kSplitRefill ? 1 : 0);
+        if constexpr (NS == 2) issue(s + NS, cur, kSplitRefill ? 1 : 0);
       }
       const int ka = kk + RD;
-      if constexpr (T::M16) {
-        // Scheduled by hand (the MFMAs are asm, which the scheduling hints do not see): one
-        // operand read of the next k step after every fourth of the step's 64 MFMAs, the B
-        // fragments first (the next step's first 8 MFMAs need all of them and A's first), and
-        // the refill loads in between.
-        const char GK_LDS* src = ka < KS ? cur : nxt;
-        const int kr = ka < KS ? ka : ka - KS;
-        Frag<T>& nf = f[(j * KS + ka) % (RD + 1)];
-        const Frag<T>& cf = f[(j * KS + kk) % (RD + 1)];
-        // refill loads of this step: at the barrier step slots [0, A_LD + B_LD/2) of panel
-        // s+2 into `cur`; at the first step the other half of B's slots of panel s+1 (into
-        // nxt; for panel 0 too, see rb_half)
-        const bool bar = kk == KS - RD, spl = kk == 0;
-        const __amdgpu_buffer_rsrc_t rA = ra_nx, rB = bar ? rb_nx : rb_half;
-        char GK_LDS* dA = bar ? cur : nxt;
-        char GK_LDS* dB = dA + T::A_BYTES;
-#pragma unroll
-        for (int i = 0; i < T::TM * T::TN; ++i) {
-          // refill loads: the barrier step's 12 every kBarGap MFMAs from MFMA kBarAt on, the
-          // first step's 4 every kSplGap from MFMA kSplAt on
-          constexpr int kBarGap = 4, kSplGap = 4, kBarAt = 2, kSplAt = 2;
-          const int gap = bar ? kBarGap : kSplGap, at = bar ? kBarAt : kSplAt;
-          if (i >= at && (i - at) % gap == 0) {
-            const int q = (i - at) / gap;
-            if (bar) {
-              if (q < T::A_LD)
-                buffer_load_lds16(rA, (void GK_LDS*)(dA + (q * OA::NW + w) * 1024), offA[q]);
-              else if (q < T::A_LD + kBHalf)
-                buffer_load_lds16(rB, (void GK_LDS*)(dB + ((q - T::A_LD) * OB::NW + w) * 1024),
-                                  offB[q - T::A_LD]);
-            } else if (spl) {
-              if (q < T::B_LD - kBHalf)
-                buffer_load_lds16(rB, (void GK_LDS*)(dB + ((kBHalf + q) * OB::NW + w) * 1024),
-                                  offB[kBHalf + q]);
-            }
-          }
-          const int tm = i / T::TN, tn = i % T::TN;
-          mfma16(acc[tm][tn], cf.a[tm], cf.b[tn]);
-          // The resources of panel s+2, for the barrier step's refill: A's after MFMA 16 of
-          // the first step, B's after MFMA 20.  The empty asms keep each piece of scalar work
-          // between two MFMAs (away from the barrier, where it would delay the next MFMA, and
-          // not in one cluster).
-          if (spl && i == 16) {
-            asm volatile("" : "+s"(qa.addr), "+s"(qa.rem));
-            ra_nx = qa.rsrc(s + NS < np);
-            qa.next();
-          }
-          if (spl && i == 20) {
-            asm volatile("" : "+s"(ra_nx), "+s"(qb.addr), "+s"(qb.rem));
-            rb_nx = qb.rsrc(s + NS < np);
-            qb.next();
-          }
-          if (spl && i == 24) asm volatile("" : "+s"(rb_nx));
-          if (i % 4 == 0 && i / 4 < T::TM + T::TN) {
-            const int r = i / 4;
-            if (r < T::TN)
-              nf.b[r] = read_operand<typename T::OB>(src, lo.b, r, kr);
-            else
-              nf.a[r - T::TN] = read_operand<typename T::OA>(src, lo.a, r - T::TN, kr);
-          }
-        }
-        if (bar) rb_half = rb_nx;
-      } else {
-        if (ka < KS)
-          read_frags<T>(f[(j * KS + ka) % (RD + 1)], cur, lo, ka);
-        else
-          read_frags<T>(f[(j * KS + ka) % (RD + 1)], nxt, lo, ka - KS);
-        mfma_step<T>(acc, f[(j * KS + kk) % (RD + 1)]);
-      }
-      if constexpr (T::M16) {
-        // scheduled above
-      } else if constexpr (NS >= 3) {
+      if (ka < KS)
+        read_frags<T>(f[(j * KS + ka) % (RD + 1)], cur, lo, ka);
+      else
+        read_frags<T>(f[(j * KS + ka) % (RD + 1)], nxt, lo, ka - KS);
+      mfma_step<T>(acc, f[(j * KS + kk) % (RD + 1)]);
+      if constexpr (NS >= 3) {
         if (kk == 0)
           sched_step<NM, ND, NV>();
         else
@@ -920,14 +838,9 @@ __device__ __forceinline__ void dma_tile(const Args& p, int m0, int n0,
       head(S[0]);
     else
       issue(0, S[0]);
-    if constexpr (T::M16) {
-      issue(1, S[1], 1);   // the rest in panel 0's first k step
-      wait_vmcnt<T::A_LD + kBHalf>();
-    } else {
 #pragma unroll
-      for (int j = 1; j < kPre; ++j) issue(j, S[j]);
-      wait_vmcnt<(kPre - 1) * NV>();
-    }
+    for (int j = 1; j < kPre; ++j) issue(j, S[j]);
+    wait_vmcnt<(kPre - 1) * NV>();
     if (has_last && np == 1) patch(S[0]);
     lds_barrier();
 #pragma unroll
@@ -941,7 +854,6 @@ __device__ __forceinline__ void dma_tile(const Args& p, int m0, int n0,
   // The last refills (of panels past the end) must land before the workgroup's LDS is freed
   // (or reused for another tile).
   wait_vmcnt<0>();
-  if constexpr (T::M16) mfma16_drain<T>(acc);
   if constexpr (SPLIT)
     store_partial<T>(p, ws, acc, m0, n0, wm, wn, lane);
   else
@@ -965,11 +877,13 @@ __device__ __forceinline__ void dma_tile(const Args& p, int m0, int n0,
 //                  loaded; A's resource of panel s+3 computed.
 // Slot indices repeat every 6 panels, so the loop is unrolled by 6 and leaves after the last
 // panel.  The k order of every element's sum is the one of the other schedules: same bits.
+// As in dma_tile, SPLIT runs panels [p0, p1) only and stores the fp32 partial into `ws`.
 // ---------------------------------------------------------------------------------------
-template <bool AKM, bool BKM>
+template <bool AKM, bool BKM, bool SPLIT = false>
 __device__ __forceinline__ void ring_tile(const Args& p, int m0, int n0,
                                           char GK_LDS* const (&SA)[3],
-                                          char GK_LDS* const (&SB)[2]) {
+                                          char GK_LDS* const (&SB)[2], int p0 = 0, int p1 = 0,
+                                          float* ws = nullptr) {
   using T = Tile<256, 256, 64, AKM, BKM, 2, 2>;
   using OA = typename T::OA;
   using OB = typename T::OB;
@@ -986,13 +900,20 @@ __device__ __forceinline__ void ring_tile(const Args& p, int m0, int n0,
   slot_offsets<OB>(offB, w, lane, p.ldb);
   const int64_t extA = extent<AKM>(p.M, p.K, p.lda);
   const int64_t extB = extent<BKM>(p.N, p.K, p.ldb);
-  const int rk = p.K % BK;                    // depth of the head panel (0: none)
-  const int np = p.K / BK + (rk ? 1 : 0);
-  const int kofs = rk ? rk - BK : 0;          // panel s covers k in [kofs + s BK, + BK)
+  const int rk0 = p.K % BK;                     // depth of the head panel (0: none)
+  const int np_all = p.K / BK + (rk0 ? 1 : 0);  // panels of the whole k range
+  // split K (see dma_tile): panels [p0, p1) renumbered from 0, the head only in the first
+  // slice, the last element's patch only in the last
+  const int np = SPLIT ? p1 - p0 : np_all;
+  const int rk = SPLIT && p0 != 0 ? 0 : rk0;
+  const bool has_last = !SPLIT || p1 == np_all;
+  // panel s covers k in [kofs + s BK, + BK)
+  const int kofs = (rk0 ? rk0 - BK : 0) + (SPLIT ? p0 * BK : 0);
   uint16_t last_a = 0, last_b = 0;
   const int patch_a = last_element_slot<OA>(m0, p.M, p.K, p.A, extA, tid, last_a);
   const int patch_b = last_element_slot<OB>(n0, p.N, p.K, p.B, extB, tid, last_b);
   auto patch = [&](char GK_LDS* a, char GK_LDS* b) __attribute__((always_inline)) {
+    if (!has_last) return;
     if (patch_a >= 0) *(uint16_t GK_LDS*)(a + patch_a) = last_a;
     if (patch_b >= 0) *(uint16_t GK_LDS*)(b + patch_b) = last_b;
   };
@@ -1107,11 +1028,34 @@ __device__ __forceinline__ void ring_tile(const Args& p, int m0, int n0,
     }
   }
   // The last refills (of panels past the end: empty resources) must land before the
-  // workgroup's LDS is freed.
+  // workgroup's LDS is freed or reused for another tile.
   wait_vmcnt<0>();
   mfma16_drain<T>(acc);
-  store_tile<T>(p, acc, m0, n0, wm, wn, lane);
+  if constexpr (SPLIT)
+    store_partial<T>(p, ws, acc, m0, n0, wm, wn, lane);
+  else
+    store_tile<T>(p, acc, m0, n0, wm, wn, lane);
 }
+
+// The five LDS slots of ring_tile: separate LDS objects, whose pointers are assigned one by
+// one (an initializer list of LDS addresses would become a static table).
+#define GK_DECLARE_RING()                                                                     \
+  __shared__ __attribute__((aligned(16))) char slot0[32768];                                  \
+  __shared__ __attribute__((aligned(16))) char slot1[32768];                                  \
+  __shared__ __attribute__((aligned(16))) char slot2[32768];                                  \
+  __shared__ __attribute__((aligned(16))) char slot3[32768];                                  \
+  __shared__ __attribute__((aligned(16))) char slot4[32768];                                  \
+  char GK_LDS* SA[3];                                                                         \
+  char GK_LDS* SB[2];                                                                         \
+  SA[0] = (char GK_LDS*)slot2;                                                                \
+  SA[1] = (char GK_LDS*)slot3;                                                                \
+  SA[2] = (char GK_LDS*)slot4;                                                                \
+  SB[0] = (char GK_LDS*)slot0;                                                                \
+  SB[1] = (char GK_LDS*)slot1;
+
+// Whether a DMA kernel's tile runs on ring_tile (the 256 x 256 x 64 tile on 2 x 2 wavefronts).
+template <int BM, int BN, int BK, int NS, int WM, int WN>
+constexpr bool kRing = BM == 256 && BN == 256 && BK == 64 && NS == 2 && WM == 2 && WN == 2;
 
 // One workgroup per program: hardware id -> program id -> tile.
 template <int BM, int BN, int BK, int NS, int RD, int WM, int WN, bool AKM, bool BKM>
@@ -1119,21 +1063,8 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_dma(Args p) {
   int pid, pid_m, pid_n;
   program_tile(blockIdx.x, p.num_programs, p.num_pid_m, p.num_pid_n, p.group_m, p.xcd_remap,
                pid, pid_m, pid_n);
-  if constexpr (Tile<BM, BN, BK, AKM, BKM, WM, WN>::M16 && NS == 2) {
-    // five separate LDS objects (see ring_tile); their pointers are assigned one by one, as
-    // an initializer list of LDS addresses would become a static table
-    __shared__ __attribute__((aligned(16))) char slot0[32768];
-    __shared__ __attribute__((aligned(16))) char slot1[32768];
-    __shared__ __attribute__((aligned(16))) char slot2[32768];
-    __shared__ __attribute__((aligned(16))) char slot3[32768];
-    __shared__ __attribute__((aligned(16))) char slot4[32768];
-    char GK_LDS* SA[3];
-    char GK_LDS* SB[2];
-    SA[0] = (char GK_LDS*)slot2;
-    SA[1] = (char GK_LDS*)slot3;
-    SA[2] = (char GK_LDS*)slot4;
-    SB[0] = (char GK_LDS*)slot0;
-    SB[1] = (char GK_LDS*)slot1;
+  if constexpr (kRing<BM, BN, BK, NS, WM, WN>) {
+    GK_DECLARE_RING()
     ring_tile<AKM, BKM>(p, pid_m * BM, pid_n * BN, SA, SB);
   } else {
     GK_DECLARE_STAGES(NS, (Tile<BM, BN, BK, AKM, BKM, WM, WN>::STAGE))
@@ -1150,13 +1081,24 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_dma(Args p) {
 // ceil(P / G) tiles.
 template <int BM, int BN, int BK, int NS, int RD, int WM, int WN, bool AKM, bool BKM>
 __global__ void __launch_bounds__(64 * WM * WN) gemm_dma_persistent(Args p) {
-  GK_DECLARE_STAGES(NS, (Tile<BM, BN, BK, AKM, BKM, WM, WN>::STAGE))
-  for (int v = blockIdx.x; v < p.num_programs; v += gridDim.x) {
-    int pid, pid_m, pid_n;
-    program_tile(v, p.num_programs, p.num_pid_m, p.num_pid_n, p.group_m, p.xcd_remap, pid,
-                 pid_m, pid_n);
-    dma_tile<BM, BN, BK, NS, RD, WM, WN, AKM, BKM>(p, pid_m * BM, pid_n * BN, S);
-    __syncthreads();   // every wave is done with the stages before the next tile's prologue
+  if constexpr (kRing<BM, BN, BK, NS, WM, WN>) {
+    GK_DECLARE_RING()
+    for (int v = blockIdx.x; v < p.num_programs; v += gridDim.x) {
+      int pid, pid_m, pid_n;
+      program_tile(v, p.num_programs, p.num_pid_m, p.num_pid_n, p.group_m, p.xcd_remap, pid,
+                   pid_m, pid_n);
+      ring_tile<AKM, BKM>(p, pid_m * BM, pid_n * BN, SA, SB);
+      __syncthreads();   // every wave is done with the slots before the next tile's prologue
+    }
+  } else {
+    GK_DECLARE_STAGES(NS, (Tile<BM, BN, BK, AKM, BKM, WM, WN>::STAGE))
+    for (int v = blockIdx.x; v < p.num_programs; v += gridDim.x) {
+      int pid, pid_m, pid_n;
+      program_tile(v, p.num_programs, p.num_pid_m, p.num_pid_n, p.group_m, p.xcd_remap, pid,
+                   pid_m, pid_n);
+      dma_tile<BM, BN, BK, NS, RD, WM, WN, AKM, BKM>(p, pid_m * BM, pid_n * BN, S);
+      __syncthreads();   // every wave is done with the stages before the next tile's prologue
+    }
   }
 }
 
@@ -1169,7 +1111,6 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_dma_persistent(Args p) {
 // fp32 partial goes to W[z].  `splitk_reduce` then adds the slices in order and narrows once.
 template <int BM, int BN, int BK, int NS, int RD, int WM, int WN, bool AKM, bool BKM>
 __global__ void __launch_bounds__(64 * WM * WN) gemm_dma_splitk(Args p) {
-  GK_DECLARE_STAGES(NS, (Tile<BM, BN, BK, AKM, BKM, WM, WN>::STAGE))
   const int z = blockIdx.x / p.num_programs;
   const int h = blockIdx.x - z * p.num_programs;
   int pid, pid_m, pid_n;
@@ -1178,8 +1119,15 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_dma_splitk(Args p) {
   const int np_all = p.K / BK + (p.K % BK ? 1 : 0);
   const int p1 = np_all - (p.splits - 1 - z) * p.panels_per_split;
   const int p0 = z == 0 ? 0 : p1 - p.panels_per_split;
-  dma_tile<BM, BN, BK, NS, RD, WM, WN, AKM, BKM, true>(
-      p, pid_m * BM, pid_n * BN, S, p0, p1, p.W + (int64_t)z * p.M * p.ldw);
+  float* const ws = p.W + (int64_t)z * p.M * p.ldw;
+  if constexpr (kRing<BM, BN, BK, NS, WM, WN>) {
+    GK_DECLARE_RING()
+    ring_tile<AKM, BKM, true>(p, pid_m * BM, pid_n * BN, SA, SB, p0, p1, ws);
+  } else {
+    GK_DECLARE_STAGES(NS, (Tile<BM, BN, BK, AKM, BKM, WM, WN>::STAGE))
+    dma_tile<BM, BN, BK, NS, RD, WM, WN, AKM, BKM, true>(p, pid_m * BM, pid_n * BN, S, p0, p1,
+                                                         ws);
+  }
 }
 
 // ---------------------------------------------------------------------------------------

@@ -85,8 +85,7 @@ enum {
  * 16-deep MFMA steps; a 32-deep 16x16x32 step sums exactly as two of them). */
 enum {
     GEMM_F16F32_TILE_AUTO = 0,
-    GEMM_F16F32_TILE_256x256x64 = 1,     /* 16x16x32 MFMAs; panels in five 32 KiB LDS slots
-                                            (2 stages in its persistent and split-K forms) */
+    GEMM_F16F32_TILE_256x256x64 = 1,     /* 16x16x32 MFMAs; panels in five 32 KiB LDS slots */
     GEMM_F16F32_TILE_128x128x64 = 2,     /* 2 stages, operands read 3 k steps ahead */
     GEMM_F16F32_TILE_128x64x64 = 3,      /* 2 stages */
     GEMM_F16F32_TILE_256x128x64 = 4,     /* 2 stages, operands read 3 k steps ahead */

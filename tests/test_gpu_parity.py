@@ -351,16 +351,17 @@ def test_persistent_schedule_changes_no_bit(M, N, K, tile):
     assert_within_tolerance(pers, oracle.gemm(A, B), f"{M}x{N}x{K}")
 
 
-# The one-workgroup-per-program 256 x 256 x 64 kernel keeps its panels in five LDS slots whose
-# indices repeat every 6 panels (A in a ring of three, B in a ring of two), and leaves its
-# unrolled loop after the last panel; its persistent form keeps the two-stage schedule.  The
-# panel counts below end at every position of the unrolled loop, with and without a head
-# panel (K not a multiple of 64), with a ragged last tile row and column, and with the
-# operands' last element patched in the last panel (odd leading dimensions).
+# The 256 x 256 x 64 kernels (one workgroup per program, persistent, split K) keep their
+# panels in five LDS slots whose indices repeat every 6 panels (A in a ring of three, B in a
+# ring of two), and leave their unrolled loop after the last panel.  The panel counts below end
+# at every position of the unrolled loop, with and without a head panel (K not a multiple of
+# 64), with a ragged last tile row and column, and with the operands' last element patched in
+# the last panel (odd leading dimensions); the split K slices start and end at other panels.
+# The 256 x 256 x 32 tile (four LDS stages, 32x32x16 MFMAs) gives the same bits.
 @pytest.mark.parametrize("K", [64, 128, 192, 256, 320, 384, 448, 768, 832, 17, 64 * 6 + 1,
                                64 * 7 + 63, 64 * 12 + 5])
 @pytest.mark.parametrize("M,N,pad", [(512, 512, 0), (300, 520, 0), (513, 257, 1)])
-def test_five_slot_schedule_equals_two_stage(M, N, K, pad):
+def test_five_slot_schedule_matches_the_staged_tile(M, N, K, pad):
     print(f"five-slot schedule {M}x{N}x{K} pad {pad}", flush=True)
     A, B = operands(M, N, K, "n(0,0.1)", M + 3 * N + 7 * K)
     Ad, Bd = to_dev(A), to_dev(B)
@@ -370,8 +371,15 @@ def test_five_slot_schedule_equals_two_stage(M, N, K, pad):
         Ap[:, :K] = Ad
         Bp[:, :N] = Bd
         Ad, Bd = Ap[:, :K], Bp[:, :N]
-    tile = g.TILE_256x256x64
-    ring = from_dev(g.matmul(Ad, Bd, tile=tile))
-    two = from_dev(g.matmul(Ad, Bd, tile=tile, persistent=g.PERSISTENT_ON))
-    assert np.array_equal(ring, two)
-    assert_within_tolerance(ring, oracle.gemm(A, B), f"{M}x{N}x{K}")
+    ring, staged = g.TILE_256x256x64, g.TILE_256x256x32
+    want = from_dev(g.matmul(Ad, Bd, tile=staged))
+    got = from_dev(g.matmul(Ad, Bd, tile=ring))
+    pers = from_dev(g.matmul(Ad, Bd, tile=ring, persistent=g.PERSISTENT_ON))
+    assert np.array_equal(got, want)
+    assert np.array_equal(pers, want)
+    ref = oracle.gemm(A, B)
+    assert_within_tolerance(got, ref, f"{M}x{N}x{K}")
+    for S in (2, 3):
+        split = from_dev(g.matmul(Ad, Bd, tile=ring, split_k=S))
+        assert np.array_equal(split, from_dev(g.matmul(Ad, Bd, tile=staged, split_k=S))), S
+        assert_within_tolerance(split, ref, f"{M}x{N}x{K} split {S}")
