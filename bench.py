@@ -7,7 +7,7 @@ HIP events recorded on the stream the kernel is launched on (torch's current str
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--all]
                     [--tile T] [--group-m G] [--xcd-remap R] [--layout AB[C]]
-                    [--layouts] [--dist D] [--vs-torch] [--no-cpu-baseline]
+                    [--layouts] [--dist D] [--vs-torch] [--no-cpu-baseline] [--floor]
 
 `value` is TFLOP/s = 2 M N K K_steps / (timed wall time); `roofline.achieved` is
 2 M N K / (mean per-launch event time), against the MI355X published dense fp16 matrix
@@ -21,6 +21,8 @@ all eight storage orders (stderr).  --dist draws the operands from another distr
 synthetic_inputs (e.g. "zeros" or "s(1/64)", which switch fewer bits in the matrix cores)
 with the workload's shape and seed; `config.dist` names the one used.  After the timed region
 the same launches run for 3 s while the XCD clocks and the socket power are sampled.
+--floor only times, in HIP-graph replays, the launches that bound the small workloads from
+below (an empty launch, K = 0, one workgroup on one panel).
 """
 from __future__ import annotations
 
@@ -218,6 +220,34 @@ def vs_torch(g, torch, name, opts, dist=None, rounds=10, block=50, warm_s=3.0):
                   "ms_max": round(max(v), 5),
                   "tflops": round(2.0 * M * N * K / (med * 1e-3) / 1e12, 1)}
     return out
+
+
+def latency_floor(torch, g):
+    """Device time per launch in HIP-graph replays of launches that bound the two small
+    workloads from below: a one-element fill (torch's, the launch alone), the library with
+    K = 0 (launch and store of a 512 x 512 C), one workgroup on one 64-deep panel (32 x 32 x
+    64: the launch, one load round trip, the store), one panel on 128 workgroups (512 x 512 x
+    64), and the two small workloads themselves.  One JSON line each on stderr."""
+    import numpy as np
+    from synthetic_inputs import operands
+
+    one = torch.empty(1, dtype=torch.float32, device="cuda")
+    us = graph_device_us(torch, lambda: one.zero_(), n=50)
+    print(json.dumps({"floor": "fill of 1 element (torch)", "graph_us_per_launch": round(us, 3)}),
+          file=sys.stderr, flush=True)
+    for M, N, K, opts, what in ((512, 512, 0, {}, "K = 0: launch and store of C"),
+                                (32, 32, 64, {}, "one workgroup, one panel"),
+                                (512, 512, 64, {}, "one panel, 128 workgroups"),
+                                (512, 512, 512, {}, "the 512^3 workload"),
+                                (1024, 768, 128, {"tile": g.TILE_128x64x64, "group_m": 2},
+                                 "the 1024 x 768 x 128 workload")):
+        A, B = operands(M, N, K, "u(-0.5,0.5)", 0)
+        Ad = torch.from_numpy(A.view(np.int16)).cuda()
+        Bd = torch.from_numpy(B.view(np.int16)).cuda()
+        Cd = torch.empty((M, N), dtype=torch.int16, device="cuda")
+        us = graph_device_us(torch, lambda: g.matmul(Ad, Bd, Cd, **opts), n=50)
+        print(json.dumps({"floor": what, "M": M, "N": N, "K": K,
+                          "graph_us_per_launch": round(us, 3)}), file=sys.stderr, flush=True)
 
 
 def copy_calibration(torch, mib, steps):
@@ -424,6 +454,9 @@ def main():
                     help="skip the 3 s clock sampling after the timed region")
     ap.add_argument("--cpu-all", action="store_true",
                     help="only time the CPU oracle on every workload (no GPU)")
+    ap.add_argument("--floor", action="store_true",
+                    help="only time, in HIP-graph replays, launches that bound the small "
+                         "workloads from below (stderr)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="only time a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -444,6 +477,9 @@ def main():
     torch.cuda.set_device(0)
     if args.copy_mib:
         copy_calibration(torch, args.copy_mib, args.steps)
+        return
+    if args.floor:
+        latency_floor(torch, g)
         return
     opts = {k: v for k, v in (("tile", args.tile), ("group_m", args.group_m),
                               ("xcd_remap", args.xcd_remap),
