@@ -34,7 +34,10 @@ def assert_same_bits(gpu, want, what):
 
 
 def run_all_ways(A, B, what):
-    """Row-major DMA path, forced generic path, and B given column-major."""
+    """Row-major DMA path, forced generic path, B given column-major, and the large tiles'
+    own kernels: the 256 x 256 x 64 tile (16x16x32 MFMAs in its five-slot schedule, also
+    persistent and split in two along k), the ping-pong tile and the four-stage 256 x 256 x 32
+    tile (32x32x16 MFMAs)."""
     M, K = A.shape
     N = B.shape[1]
     want = oracle.gemm(A, B)
@@ -43,6 +46,13 @@ def run_all_ways(A, B, what):
     assert_same_bits(from_dev(g.matmul(Ad, Bd, force_generic=1)), want, what + " generic")
     Bt = to_dev(np.ascontiguousarray(B.T)).t()
     assert_same_bits(from_dev(g.matmul(Ad, Bt)), want, what + " B column-major")
+    for t in (g.TILE_256x256x64, g.TILE_256x256x32_PP, g.TILE_256x256x32):
+        assert_same_bits(from_dev(g.matmul(Ad, Bd, tile=t)), want, f"{what} tile {t}")
+    t1 = g.TILE_256x256x64
+    assert_same_bits(from_dev(g.matmul(Ad, Bd, tile=t1, persistent=g.PERSISTENT_ON)), want,
+                     what + " persistent")
+    # two slices when K > 128; the slices' fp32 sums are exact here too, so their sum is
+    assert_same_bits(from_dev(g.matmul(Ad, Bd, tile=t1, split_k=2)), want, what + " split")
     return want
 
 
@@ -121,3 +131,30 @@ def test_signed_zero():
     B = np.full((K, N), h(1.0), np.uint16)
     B[: K // 2] = h(-1.0)
     assert np.all(run_all_ways(A, B, "cancellation") == 0)
+
+
+def test_special_values_across_split_k_slices():
+    """K = 300 in two slices (k < 44 and k >= 44, each summed in fp32, then added): an
+    infinity in each slice of opposite signs gives NaN, of the same sign infinity; a NaN in
+    one slice wins; a slice sum beyond fp16's range with a finite total of the other slice
+    still overflows on the one narrowing; values cancelling across slices give +0."""
+    M, N, K = 70, 90, 300
+    A = np.full((M, K), h(0.5), np.uint16)
+    B = np.full((K, N), h(0.25), np.uint16)
+    A[1, 3], A[1, 200] = INF, NINF           # row 1: +inf (slice 0) and -inf (slice 1): NaN
+    A[2, 3], A[2, 200] = INF, INF            # row 2: +inf
+    A[3, 250] = NAN                          # row 3: NaN from slice 1
+    A[4, :] = h(2047.0)                      # row 4: 300 x 2047 x 0.25 = 153525: +inf
+    A[5, :] = h(1.0)
+    A[5, 44:] = h(-1.0)                      # row 5 with column 7 all ones: 44 - 256
+    B[:, 7] = h(1.0)
+    A[6, :44] = h(64.0)                      # row 6: 64 x 44 - 11.0 x 256, column 7: 0
+    A[6, 44:] = h(-11.0)
+    want = run_all_ways(A, B, "split slices")
+    rc, info = g.gemm_f16f32_plan(M, N, K, 1 << 40, 2 << 40, 3 << 40, K, N, N,
+                                  opts={"tile": g.TILE_256x256x64, "split_k": 2})
+    assert rc == g.OK and info["splits"] == 2 and info["split_depth"] == 256
+    nan = lambda v: (v & 0x7C00) == 0x7C00 and (v & 0x3FF) != 0
+    assert all(nan(v) for v in want[1]) and np.all(want[2] == INF)
+    assert all(nan(v) for v in want[3]) and np.all(want[4] == INF)
+    assert want[5, 7] == h(44.0 - 256.0) and want[6, 7] == 0
