@@ -862,7 +862,8 @@ __device__ __forceinline__ void dma_tile(const Args& p, int m0, int n0,
 
 // ---------------------------------------------------------------------------------------
 // The 256 x 256 x 64 tile on 16x16x32 MFMAs (one workgroup per program, each tile of the
-// persistent schedule, and the split-K slices): the operand panels in five LDS slots of 32 KiB (all 160 KiB), A's in a ring of three and B's in a ring of two.
+// persistent schedule, and the split-K slices): the operand panels in five LDS slots of 32 KiB
+// (all 160 KiB), A's in a ring of three and B's in a ring of two.
 // With two 64 KiB stages a panel's whole refill can only start at the barrier that frees its
 // stage; here A of panel s+2 goes to the slot that held A of panel s-1 -- free since panel
 // s-1's barrier -- and is loaded during panel s's first k step, and B of panel s+2 goes to
