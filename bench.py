@@ -8,6 +8,7 @@ HIP events recorded on the stream the kernel is launched on (torch's current str
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--all]
                     [--tile T] [--group-m G] [--xcd-remap R] [--layout AB[C]]
                     [--layouts] [--dist D] [--vs-torch] [--no-cpu-baseline] [--floor]
+                    [--mfma-ceiling]
 
 `value` is TFLOP/s = 2 M N K K_steps / (timed wall time); `roofline.achieved` is
 2 M N K / (mean per-launch event time), against the MI355X published dense fp16 matrix
@@ -22,7 +23,8 @@ synthetic_inputs (e.g. "zeros" or "s(1/64)", which switch fewer bits in the matr
 with the workload's shape and seed; `config.dist` names the one used.  After the timed region
 the same launches run for 3 s while the XCD clocks and the socket power are sampled.
 --floor only times, in HIP-graph replays, the launches that bound the small workloads from
-below (an empty launch, K = 0, one workgroup on one panel).
+below (an empty launch, K = 0, one workgroup on one panel).  --mfma-ceiling only times the
+matrix-core rate probe: the 8192^3 GEMM's MFMAs from registers, with no memory traffic.
 """
 from __future__ import annotations
 
@@ -250,6 +252,61 @@ def latency_floor(torch, g):
                           "graph_us_per_launch": round(us, 3)}), file=sys.stderr, flush=True)
 
 
+def mfma_ceiling(torch, dist, steps, warmup, clocks):
+    """The matrix cores alone (dense_gemm_f16f32_amd/libmfma_ceiling.so, the rate probe):
+    each launch issues the 8192^3 GEMM's 2^26 v_mfma_f32_16x16x32_f16 on the GEMM's grid and
+    in its operand pattern, from registers only, on operands uniform on [-0.5, 0.5) or all
+    +0 (dist "zeros").  Timed like the GEMM (W warm-up launches, K timed ones, per-launch
+    events) and followed by the same clock and power sampling; one JSON line on stdout."""
+    import ctypes
+
+    if dist not in (None, "zeros", "u(-0.5,0.5)"):
+        raise SystemExit("--mfma-ceiling takes --dist zeros or the default u(-0.5,0.5)")
+    lib = ctypes.CDLL(os.path.join(ROOT, "dense_gemm_f16f32_amd", "libmfma_ceiling.so"))
+    f = lib.mfma_ceiling_launch
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_uint32,
+                  ctypes.c_void_p]
+    blocks, iters = 256, 512        # 1024 wavefronts x 512 x 128 MFMAs = 2^26
+    flops = blocks * 4 * iters * 128 * (2 * 16 * 16 * 32)
+    out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def launch():
+        rc = f(out.data_ptr(), blocks, iters, 1 if dist == "zeros" else 0, 3, stream.cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"mfma_ceiling_launch: hipError {rc}")
+
+    for _ in range(warmup):
+        launch()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    t0 = time.perf_counter()
+    for a, b in ev:
+        a.record(stream)
+        launch()
+        b.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = sorted(a.elapsed_time(b) for a, b in ev)
+    mean = sum(ms) / len(ms)
+    achieved = flops / (mean * 1e-3) / 1e12
+    res = {"probe": "mfma_ceiling", "dist": dist or "u(-0.5,0.5)", "mfmas_per_launch": 1 << 26,
+           "steps": steps, "warmup": warmup, "value": round(flops * steps / wall / 1e12, 2),
+           "achieved": round(achieved, 2), "peak": PEAK_TFLOPS,
+           "frac": round(achieved / PEAK_TFLOPS, 4),
+           "kernel_ms": {"mean": round(mean, 5), "median": round(ms[len(ms) // 2], 5),
+                         "min": round(ms[0], 5)}}
+    if clocks:
+        c = sample_clocks(None, torch, launch)
+        if c:
+            peak = 256 * 4096 * c["median"] * 1e6 / 1e12
+            res.update(sclk_mhz=c, peak_at_sclk=round(peak, 1),
+                       frac_at_sclk=round(achieved / peak, 4))
+    print(json.dumps(res), flush=True)
+
+
 def copy_calibration(torch, mib, steps):
     """A plain device copy of known size, timed; profiled with the same HBM counters as the
     GEMM it gives the factor between counter readings and bytes actually moved."""
@@ -454,6 +511,9 @@ def main():
                     help="skip the 3 s clock sampling after the timed region")
     ap.add_argument("--cpu-all", action="store_true",
                     help="only time the CPU oracle on every workload (no GPU)")
+    ap.add_argument("--mfma-ceiling", action="store_true",
+                    help="only time the matrix-core rate probe (the GEMM's MFMAs from "
+                         "registers, no memory traffic) on --dist zeros or the default data")
     ap.add_argument("--floor", action="store_true",
                     help="only time, in HIP-graph replays, launches that bound the small "
                          "workloads from below (stderr)")
@@ -480,6 +540,9 @@ def main():
         return
     if args.floor:
         latency_floor(torch, g)
+        return
+    if args.mfma_ceiling:
+        mfma_ceiling(torch, args.dist, args.steps, args.warmup, not args.no_clocks)
         return
     opts = {k: v for k, v in (("tile", args.tile), ("group_m", args.group_m),
                               ("xcd_remap", args.xcd_remap),

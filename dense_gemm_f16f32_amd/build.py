@@ -13,6 +13,9 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 SRC = os.path.join(PKG, "csrc", "gemm_f16f32.hip")
 SO = os.path.join(PKG, "libgemm_f16f32.so")
+# The matrix-core rate probe (measurement only: bench.py --mfma-ceiling).
+PROBE_SRC = os.path.join(PKG, "csrc", "mfma_ceiling.hip")
+PROBE_SO = os.path.join(PKG, "libmfma_ceiling.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
@@ -50,7 +53,8 @@ def kernel_source_hash() -> str:
 # Kernels whose 16x16x32 MFMAs are inline asm (the 256 x 256 x 64 tile on 2 x 2 wavefronts:
 # its DMA, persistent, split-K and generic forms).  The compiler's hazard checks do not see
 # those MFMAs, so the code provides the wait states itself (gemm_kernels.hpp, mfma16).
-ASM_MFMA_KERNELS = ("ILi256ELi256ELi64ELi2ELi1ELi2ELi2E",   # gemm_dma*, tile 1
+ASM_MFMA_KERNELS = ("mfma_ceiling",                         # the rate probe
+                    "ILi256ELi256ELi64ELi2ELi1ELi2ELi2E",   # gemm_dma*, tile 1
                     "gemm_genericILi256ELi256ELb")          # gemm_generic, 256 x 256 tiles
 
 
@@ -142,7 +146,22 @@ def build(extra=()) -> str:
         os.remove(tmp)
         raise RuntimeError("no asm-MFMA kernel found to check in the built library")
     os.replace(tmp, SO)
+    build_probe()
     return SO
+
+
+def build_probe() -> str:
+    """Compiles the matrix-core rate probe (a library of its own, for bench.py only)."""
+    tmp = PROBE_SO + ".tmp"
+    r = subprocess.run([HIPCC, *FLAGS, PROBE_SRC, "-o", tmp], capture_output=True, text=True)
+    msgs = [ln for ln in (r.stdout + r.stderr).splitlines() if "packed-fp32-ops" not in ln]
+    if r.returncode != 0:
+        raise RuntimeError("hipcc failed on the probe:\n" + "\n".join(msgs))
+    if check_mfma_waits(tmp) != 1:
+        os.remove(tmp)
+        raise RuntimeError("the probe's asm-MFMA kernel was not found to check")
+    os.replace(tmp, PROBE_SO)
+    return PROBE_SO
 
 
 if __name__ == "__main__":

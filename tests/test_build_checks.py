@@ -5,7 +5,7 @@ not see; the code waits 32 states after the last MFMA before the accumulators ar
 after zeroing them before the first MFMA.  dense_gemm_f16f32_amd/build.py scans the built
 gfx950 code for any accumulator move the compiler might place between them.  Checked here: the
 scan flags both kinds of violation in a hand-written listing, accepts the pattern the kernels
-use, and passes on the built library.
+use, and passes on the built library and on the matrix-core rate probe built beside it.
 """
 import os
 
@@ -56,3 +56,13 @@ def test_built_library_meets_the_waits():
     if not os.path.exists(b.SO):
         pytest.skip("library not built")
     assert b.check_mfma_waits(b.SO) >= 8
+
+
+def test_built_rate_probe_meets_the_waits_and_exports_its_launcher():
+    """The matrix-core rate probe (bench.py --mfma-ceiling) is built beside the library, with
+    the same wait states around its asm MFMAs."""
+    if not os.path.exists(b.PROBE_SO):
+        pytest.skip("probe not built")
+    assert b.check_mfma_waits(b.PROBE_SO) == 1
+    import ctypes
+    assert hasattr(ctypes.CDLL(b.PROBE_SO), "mfma_ceiling_launch")
