@@ -134,7 +134,7 @@ struct Tile {
   static constexpr int WM = WM_, WN = WN_, NW = WM * WN, NT = 64 * NW;  // waves, threads
   // The 256 x 256 x 64 tile on 2 x 2 wavefronts issues 16x16x32 MFMAs (see ring_tile and,
   // for its generic form, gemm_generic): on random operands that instruction does more work
-  // per joule, and large GEMMs run at the board's power cap.  Every other tile keeps 32x32x16.
+  // per joule, and large GEMMs run at the chip's power limit.  Every other tile keeps 32x32x16.
   static constexpr bool M16 = BM_ == 256 && BN_ == 256 && BK_ == 64 && WM_ == 2 && WN_ == 2;
   static constexpr int XB = M16 ? 16 : 32, KD = M16 ? 32 : 16, VN = M16 ? 4 : 16;
   using Acc = std::conditional_t<M16, float4v, float16v>;
