@@ -77,3 +77,17 @@ def test_mfma_ceiling_probe_reports_its_rate(dist):
     assert out["steps"] == 3 and out["warmup"] == 1 and out["peak"] == 2500.0
     assert 0 < out["frac"] < 1 and abs(out["frac"] - out["achieved"] / out["peak"]) < 1e-4
     assert 0 < out["kernel_ms"]["min"] <= out["kernel_ms"]["median"]
+
+
+def test_latency_floor_lists_its_launches():
+    """bench.py --floor: one stderr line per launch it times, each with a positive device time
+    per launch from graph replays; nothing on stdout."""
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--floor"],
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stderr[-2000:]
+    assert not r.stdout.strip()
+    lines = [json.loads(ln) for ln in r.stderr.splitlines() if ln.startswith('{"floor"')]
+    assert len(lines) == 6, r.stderr[-2000:]
+    assert all(d["graph_us_per_launch"] > 0 for d in lines)
+    assert [(d.get("M"), d.get("N"), d.get("K")) for d in lines[1:]] == [
+        (512, 512, 0), (32, 32, 64), (512, 512, 64), (512, 512, 512), (1024, 768, 128)]
