@@ -463,7 +463,9 @@ int launch_part(const Problem& pr, const Part& pt, float* ws, hipStream_t s) {
   a.K = (int32_t)pr.K;
   a.num_pid_m = r.num_pid_m;
   a.num_pid_n = r.num_pid_n;
-  a.group_m = r.group_m;
+  // A group of G >= num_pid_m tile rows maps every program as G = num_pid_m does; passing at
+  // most num_pid_m keeps G * num_pid_n (<= the program count) inside the kernels' 32 bits.
+  a.group_m = r.group_m < r.num_pid_m ? r.group_m : r.num_pid_m;
   a.xcd_remap = r.xcd_remap;
   a.num_programs = r.num_programs;
   a.W = ws;
@@ -658,7 +660,8 @@ int gemm_f16f32_tile_map(int32_t num_pid_m, int32_t num_pid_n, int32_t group_m,
   if (group_m < 1 || xcd_remap < 0 || xcd_remap > 2) return GEMM_F16F32_ERR_OPTS;
   if (out_dev == nullptr) return GEMM_F16F32_ERR_NULL;
   hipLaunchKernelGGL(gk::tile_map_kernel, dim3((uint32_t)P), dim3(64), 0, (hipStream_t)stream,
-                     (int)P, num_pid_m, num_pid_n, group_m, xcd_remap == 1 ? 1 : 0, out_dev);
+                     (int)P, num_pid_m, num_pid_n, group_m < num_pid_m ? group_m : num_pid_m,
+                     xcd_remap == 1 ? 1 : 0, out_dev);
   return hipGetLastError() == hipSuccess ? GEMM_F16F32_OK : GEMM_F16F32_ERR_HIP;
 }
 

@@ -33,12 +33,32 @@ def _sync_after():
 # Tile map: bit-exact against the oracle's grouped map and XCD permutation.
 # ---------------------------------------------------------------------------------------
 @pytest.mark.parametrize("m,n,G", [(8, 12, 2), (16, 16, 8), (16, 17, 6), (32, 32, 8), (1, 1, 1),
-                                   (3, 7, 5), (40, 33, 7), (5, 3, 3), (64, 64, 4)])
+                                   (3, 7, 5), (40, 33, 7), (5, 3, 3), (64, 64, 4),
+                                   # large grids and divisors: the map divides by G num_pid_n,
+                                   # G and the last group's rows with multiply-and-shift
+                                   (1021, 1031, 13), (3, 200001, 2), (700, 3, 1 << 30),
+                                   (50000, 41, 7), (46341, 3, 46339)])
 @pytest.mark.parametrize("remap", [g.REMAP_ON, g.REMAP_OFF])
 def test_tile_map_bit_exact(m, n, G, remap):
     got = g.tile_map(m, n, G, remap).cpu().numpy().astype(np.int64)
     want = oracle.program_tiles(m, n, G, remap == g.REMAP_ON)
     assert np.array_equal(got, want)
+
+
+def test_huge_group_m_maps_like_one_group():
+    """GROUP_SIZE_M beyond the tile rows -- here 2^30, whose product with the 25 tile columns
+    would not fit in 32 bits -- maps every program as one group of all the rows does."""
+    M, N, K = 600, 800, 96
+    A, B = operands(M, N, K, "n(0,0.1)", 17)
+    Ad, Bd = to_dev(A), to_dev(B)
+    t = g.TILE_32x32x64
+    rc, info = g.gemm_f16f32_plan(M, N, K, 1 << 40, 2 << 40, 3 << 40, K, N, N,
+                                  opts={"tile": t, "group_m": 1 << 30})
+    assert rc == g.OK and info["group_m"] == 1 << 30 and info["num_pid_n"] == 25
+    huge = from_dev(run(Ad, Bd, M, N, K, tile=t, group_m=1 << 30))
+    whole = from_dev(run(Ad, Bd, M, N, K, tile=t, group_m=info["num_pid_m"]))
+    assert np.array_equal(huge, whole)
+    assert_within_tolerance(huge, oracle.gemm(A, B), "group_m 2^30")
 
 
 def test_tile_map_worked_example():
