@@ -8,7 +8,7 @@ HIP events recorded on the stream the kernel is launched on (torch's current str
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--all]
                     [--tile T] [--group-m G] [--xcd-remap R] [--layout AB[C]]
                     [--layouts] [--dist D] [--vs-torch] [--no-cpu-baseline] [--floor]
-                    [--mfma-ceiling]
+                    [--mfma-ceiling [--mfma-shape S]]
 
 `value` is TFLOP/s = 2 M N K K_steps / (timed wall time); `roofline.achieved` is
 2 M N K / (mean per-launch event time), against the MI355X published dense fp16 matrix
@@ -24,7 +24,8 @@ with the workload's shape and seed; `config.dist` names the one used.  After the
 the same launches run for 3 s while the XCD clocks and the socket power are sampled.
 --floor only times, in HIP-graph replays, the launches that bound the small workloads from
 below (an empty launch, K = 0, one workgroup on one panel).  --mfma-ceiling only times the
-matrix-core rate probe: the 8192^3 GEMM's MFMAs from registers, with no memory traffic.
+matrix-core rate probe: the 8192^3 GEMM's MFMAs from registers, with no memory traffic
+(--mfma-shape 32x32x16: the same flops in the other fp16 MFMA shape, for comparison).
 """
 from __future__ import annotations
 
@@ -252,12 +253,17 @@ def latency_floor(torch, g):
                           "graph_us_per_launch": round(us, 3)}), file=sys.stderr, flush=True)
 
 
-def mfma_ceiling(torch, dist, steps, warmup, clocks):
+MFMA_SHAPES = {"16x16x32": 0, "32x32x16": 1}
+
+
+def mfma_ceiling(torch, dist, steps, warmup, clocks, shape="16x16x32"):
     """The matrix cores alone (dense_gemm_f16f32_amd/libmfma_ceiling.so, the rate probe):
     each launch issues the 8192^3 GEMM's 2^26 v_mfma_f32_16x16x32_f16 on the GEMM's grid and
     in its operand pattern, from registers only, on operands uniform on [-0.5, 0.5) or all
-    +0 (dist "zeros").  Timed like the GEMM (W warm-up launches, K timed ones, per-launch
-    events) and followed by the same clock and power sampling; one JSON line on stdout."""
+    +0 (dist "zeros").  With shape "32x32x16" it issues the same flops as 2^25
+    v_mfma_f32_32x32x16_f16 instead.  Timed like the GEMM (W warm-up launches, K timed ones,
+    per-launch events) and followed by the same clock and power sampling; one JSON line on
+    stdout."""
     import ctypes
 
     if dist not in (None, "zeros", "u(-0.5,0.5)"):
@@ -265,15 +271,18 @@ def mfma_ceiling(torch, dist, steps, warmup, clocks):
     lib = ctypes.CDLL(os.path.join(ROOT, "dense_gemm_f16f32_amd", "libmfma_ceiling.so"))
     f = lib.mfma_ceiling_launch
     f.restype = ctypes.c_int
-    f.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_uint32,
-                  ctypes.c_void_p]
-    blocks, iters = 256, 512        # 1024 wavefronts x 512 x 128 MFMAs = 2^26
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                  ctypes.c_uint32, ctypes.c_void_p]
+    if shape not in MFMA_SHAPES:
+        raise SystemExit("--mfma-shape takes " + " or ".join(MFMA_SHAPES))
+    blocks, iters = 256, 512        # 1024 wavefronts x 512 x 128 MFMAs of 16x16x32 = 2^26
     flops = blocks * 4 * iters * 128 * (2 * 16 * 16 * 32)
     out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
 
     def launch():
-        rc = f(out.data_ptr(), blocks, iters, 1 if dist == "zeros" else 0, 3, stream.cuda_stream)
+        rc = f(out.data_ptr(), blocks, iters, MFMA_SHAPES[shape], 1 if dist == "zeros" else 0, 3,
+               stream.cuda_stream)
         if rc != 0:
             raise RuntimeError(f"mfma_ceiling_launch: hipError {rc}")
 
@@ -292,7 +301,9 @@ def mfma_ceiling(torch, dist, steps, warmup, clocks):
     ms = sorted(a.elapsed_time(b) for a, b in ev)
     mean = sum(ms) / len(ms)
     achieved = flops / (mean * 1e-3) / 1e12
-    res = {"probe": "mfma_ceiling", "dist": dist or "u(-0.5,0.5)", "mfmas_per_launch": 1 << 26,
+    res = {"probe": "mfma_ceiling", "mfma": f"v_mfma_f32_{shape}_f16",
+           "dist": dist or "u(-0.5,0.5)",
+           "mfmas_per_launch": 1 << 26 if shape == "16x16x32" else 1 << 25,
            "steps": steps, "warmup": warmup, "value": round(flops * steps / wall / 1e12, 2),
            "achieved": round(achieved, 2), "peak": PEAK_TFLOPS,
            "frac": round(achieved / PEAK_TFLOPS, 4),
@@ -514,6 +525,8 @@ def main():
     ap.add_argument("--mfma-ceiling", action="store_true",
                     help="only time the matrix-core rate probe (the GEMM's MFMAs from "
                          "registers, no memory traffic) on --dist zeros or the default data")
+    ap.add_argument("--mfma-shape", default="16x16x32",
+                    help="with --mfma-ceiling: 16x16x32 (the GEMM's MFMAs) or 32x32x16")
     ap.add_argument("--floor", action="store_true",
                     help="only time, in HIP-graph replays, launches that bound the small "
                          "workloads from below (stderr)")
@@ -542,7 +555,8 @@ def main():
         latency_floor(torch, g)
         return
     if args.mfma_ceiling:
-        mfma_ceiling(torch, args.dist, args.steps, args.warmup, not args.no_clocks)
+        mfma_ceiling(torch, args.dist, args.steps, args.warmup, not args.no_clocks,
+                     args.mfma_shape)
         return
     opts = {k: v for k, v in (("tile", args.tile), ("group_m", args.group_m),
                               ("xcd_remap", args.xcd_remap),

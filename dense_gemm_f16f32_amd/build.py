@@ -53,7 +53,7 @@ def kernel_source_hash() -> str:
 # Kernels whose 16x16x32 MFMAs are inline asm (the 256 x 256 x 64 tile on 2 x 2 wavefronts:
 # its DMA, persistent, split-K and generic forms).  The compiler's hazard checks do not see
 # those MFMAs, so the code provides the wait states itself (gemm_kernels.hpp, mfma16).
-ASM_MFMA_KERNELS = ("mfma_ceiling",                         # the rate probe
+ASM_MFMA_KERNELS = ("mfma_ceiling",                         # the rate probe (both)
                     "ILi256ELi256ELi64ELi2ELi1ELi2ELi2E",   # gemm_dma*, tile 1
                     "gemm_genericILi256ELi256ELb")          # gemm_generic, 256 x 256 tiles
 
@@ -157,9 +157,9 @@ def build_probe() -> str:
     msgs = [ln for ln in (r.stdout + r.stderr).splitlines() if "packed-fp32-ops" not in ln]
     if r.returncode != 0:
         raise RuntimeError("hipcc failed on the probe:\n" + "\n".join(msgs))
-    if check_mfma_waits(tmp) != 1:
+    if check_mfma_waits(tmp) != 2:
         os.remove(tmp)
-        raise RuntimeError("the probe's asm-MFMA kernel was not found to check")
+        raise RuntimeError("the probe's two asm-MFMA kernels were not found to check")
     os.replace(tmp, PROBE_SO)
     return PROBE_SO
 

@@ -67,12 +67,15 @@ def test_vs_torch_reports_both_sides():
         assert abs(t["tflops"] - 2 * 4096 ** 3 / (t["ms_median"] * 1e-3) / 1e12) < 0.1 + 1e-3 * t["tflops"]
 
 
+@pytest.mark.parametrize("shape", ["16x16x32", "32x32x16"])
 @pytest.mark.parametrize("dist", [[], ["--dist", "zeros"]], ids=["u", "zeros"])
-def test_mfma_ceiling_probe_reports_its_rate(dist):
-    """bench.py --mfma-ceiling: the rate probe's 2^26 MFMAs per launch, a rate below the
-    nominal peak, and frac = achieved / peak."""
-    out = run_bench("--mfma-ceiling", "--steps", "3", "--warmup", "1", "--no-clocks", *dist)
-    assert out["probe"] == "mfma_ceiling" and out["mfmas_per_launch"] == 1 << 26
+def test_mfma_ceiling_probe_reports_its_rate(dist, shape):
+    """bench.py --mfma-ceiling: the rate probe's MFMAs per launch (2^26 of 16x16x32 or the same
+    flops as 2^25 of 32x32x16), a rate below the nominal peak, and frac = achieved / peak."""
+    out = run_bench("--mfma-ceiling", "--mfma-shape", shape, "--steps", "3", "--warmup", "1",
+                    "--no-clocks", *dist)
+    assert out["probe"] == "mfma_ceiling" and out["mfma"] == f"v_mfma_f32_{shape}_f16"
+    assert out["mfmas_per_launch"] == (1 << 26 if shape == "16x16x32" else 1 << 25)
     assert out["dist"] == ("zeros" if dist else "u(-0.5,0.5)")
     assert out["steps"] == 3 and out["warmup"] == 1 and out["peak"] == 2500.0
     assert 0 < out["frac"] < 1 and abs(out["frac"] - out["achieved"] / out["peak"]) < 1e-4
